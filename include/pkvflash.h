@@ -1,0 +1,204 @@
+/*
+ * pkvflash.h -- C ABI of the paged-KV FlashAttention library for MI355X (gfx950).
+ *
+ * Three operations, following the calls the "FlashAttention deep dive" page
+ * (vLLM V1 FlashAttention backend) describes:
+ *   pkv_cache_write        -- the KV-cache update by slot_mapping (core
+ *                             implementation section, KV cache update);
+ *   pkv_varlen_fwd         -- the varlen attention forward over a paged cache
+ *                             addressed by a block table (core implementation
+ *                             section, the varlen forward and its arguments);
+ *                             semantics of the packed batch, the causal mask,
+ *                             the online softmax, paging and split-KV follow
+ *                             "How vLLM attention kernels handle multiple
+ *                             requests in parallel", sections 1-12;
+ *   pkv_merge_attn_states  -- the log-sum-exp merge of two attention states
+ *                             (cascade attention section).
+ *
+ * Conventions for every call:
+ *  - Every pointer argument is a DEVICE pointer unless stated otherwise; the
+ *    caller owns every buffer. The library never allocates device memory,
+ *    never synchronises the device and only enqueues work on `stream` (a
+ *    hipStream_t; NULL is the default stream). Calls are therefore safe to
+ *    capture into a HIP graph.
+ *  - Tensors are dense and row-major in the layouts given below.
+ *  - Arguments are validated on the host before anything is launched; on error
+ *    nothing is enqueued, the return value names the class of error and
+ *    pkv_last_error() gives a message (thread-local, valid until the next call
+ *    on that thread).
+ *  - Integer metadata (query_start_loc, seq_lens, block_table) lives on the
+ *    device; its host-side summaries (num_tokens, max_seqlen_q, max_seqlen_k)
+ *    size the launch so no device-to-host copy is needed. Values on the device
+ *    that contradict them give undefined results.
+ */
+#ifndef PKVFLASH_H
+#define PKVFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = 1,  /* a null pointer, a negative or inconsistent size */
+    PKV_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (dtype pair, head size) */
+    PKV_ERR_WORKSPACE = 3,    /* the split-KV workspace is missing or too small */
+    PKV_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+/* Element types. PKV_FP8_E4M3FN is the OCP 8-bit float E4M3 ("fn": no
+ * infinities, NaN = S.1111.111), the float8_e4m3fn type the deep-dive page's
+ * FP8 section maps the "fp8" / "fp8_e4m3" cache dtypes to. */
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3FN = 2 } pkv_dtype;
+
+/* ------------------------------------------------------------------ cache write
+ * For each new token t in [0, num_tokens):
+ *   slot = slot_mapping[t]; if slot < 0 the token is padding and is skipped;
+ *   block = slot / block_size, offset = slot % block_size;
+ *   k_cache[block][offset][h][d] = enc(key[t][h][d]), likewise value -> v_cache.
+ * Layouts: key, value [num_tokens, num_kv_heads, head_size] in src_dtype;
+ *          k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_size]
+ *          in cache_dtype (the K and V halves of the backend's
+ *          (2, num_blocks, block_size, num_kv_heads, head_size) cache).
+ *          slot_mapping [num_tokens] int64.
+ * enc: same type -> bit copy; F32 -> BF16 round to nearest even;
+ *      F32 or BF16 -> FP8_E4M3FN: y = x / scale as a correctly rounded binary32
+ *      division by the per-tensor scale (*k_scale or *v_scale, device fp32
+ *      scalars), then the nearest E4M3FN value, ties to even; |y| >= 448 and
+ *      +-inf saturate to +-448; NaN gives 0x7F with the sign of y.
+ * k_scale / v_scale are read only for an FP8 cache (may be NULL otherwise).
+ * Two tokens with the same slot give an undefined result; every slot must be
+ * < num_blocks * block_size (not checked on the device).
+ * Errors: INVALID_ARG for null pointers or non-positive sizes, UNSUPPORTED for
+ * other type pairs (BF16 -> F32, FP8 sources). num_tokens == 0 is a no-op.    */
+pkv_status pkv_cache_write(const void* key, const void* value, pkv_dtype src_dtype,
+                           void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                           const int64_t* slot_mapping, int64_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                           int64_t num_blocks, const float* k_scale, const float* v_scale,
+                           void* stream);
+
+/* --------------------------------------------------------------- varlen forward
+ * Attention over a packed batch of num_seqs requests. Request r owns query
+ * tokens [query_start_loc[r], query_start_loc[r+1]) (q_len_r of them) and a KV
+ * sequence of seq_lens[r] tokens that INCLUDES its q_len_r new tokens (their
+ * K/V must already be in the cache: the cache write runs first). With
+ * ctx_r = seq_lens[r] - q_len_r, query t of request r (request-local index)
+ * sees keys 0 .. ctx_r + t when causal (bottom-right aligned mask, as in the
+ * multi-token verification section), and every key 0 .. seq_lens[r]-1 when not.
+ * Query head h reads kv head h / (num_heads / num_kv_heads) (GQA groups of
+ * consecutive heads). Key j of request r is found through the block table:
+ * block = block_table[r * block_table_stride + j / block_size], row
+ * j % block_size of that block (paged address translation, section 11).
+ *
+ *   out[t][h] = sum_j softmax_j(softmax_scale * q[t][h] . k_j) v_j
+ *   lse[h][t] = log(sum_j exp(softmax_scale * q[t][h] . k_j))   (natural log)
+ * A row with no visible key gets out = 0 and lse = -inf.
+ *
+ * Layouts: q, out [num_tokens, num_heads, head_size] in q_dtype (out has the
+ *          type of q); lse [num_heads, num_tokens] fp32, or NULL;
+ *          k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_size]
+ *          in kv_dtype; block_table int32 rows of block_table_stride entries
+ *          (a row may be a strided view: pass the address of its first used
+ *          entry and the stride of the full table); query_start_loc [num_seqs+1]
+ *          and seq_lens [num_seqs] int32.
+ * Flat mode: block_table == NULL means K and V are not paged: k_cache and
+ *          v_cache are [num_tokens, num_kv_heads, head_size] packed like q and
+ *          each request attends to its own new tokens only (seq_lens may be
+ *          NULL; it is then taken as q_len).
+ * Types:   q_dtype BF16 with kv_dtype BF16 or FP8_E4M3FN; F32 with F32.
+ *          FP8 keys/values are multiplied by *k_scale / *v_scale (device fp32).
+ * Head size: a multiple of 8, at most 256 (the deep-dive page's backend rule).
+ * Split-KV: num_splits 0 lets the library choose from the host sizes, 1 turns
+ *          splitting off, > 1 asks for that many KV splits (at most 256). With
+ *          more than one split the partial results (one per split) go to the
+ *          workspace and a second kernel merges them by log-sum-exp
+ *          (section 12); pkv_varlen_workspace_size gives the bytes needed.  */
+typedef struct pkv_varlen_args {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    void* out;
+    float* lse;
+    const int32_t* query_start_loc;
+    const int32_t* seq_lens;
+    const int32_t* block_table;
+    const float* k_scale;
+    const float* v_scale;
+    void* workspace;
+    size_t workspace_bytes;
+    int64_t block_table_stride;
+    int64_t num_blocks;
+    int64_t num_tokens;     /* query_start_loc[num_seqs], as a host integer */
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t head_size;
+    int32_t block_size;
+    int32_t max_seqlen_q;   /* >= every q_len_r */
+    int32_t max_seqlen_k;   /* >= every seq_lens[r] */
+    int32_t num_splits;
+    int32_t causal;
+    int32_t q_dtype;        /* pkv_dtype */
+    int32_t kv_dtype;       /* pkv_dtype */
+    float softmax_scale;
+} pkv_varlen_args;
+
+/* sizeof(pkv_varlen_args), so bindings can check their mirror of the struct. */
+size_t pkv_varlen_args_size(void);
+
+/* Validate `a` on the host only (no device access, no launch). */
+pkv_status pkv_varlen_check(const pkv_varlen_args* a);
+
+/* Number of KV splits pkv_varlen_fwd will use for `a` (1 when no split is
+ * needed; 0 if the sizes in `a` are invalid), and the workspace bytes that
+ * needs. Only the sizes, types and block_table/NULL choice of `a` are read:
+ * the data pointers may be NULL here. The workspace
+ * holds fp32 partial outputs [splits, num_tokens, num_heads, head_size] and
+ * partial lse [splits, num_heads, num_tokens]; it is caller-owned and may be
+ * reused between calls on one stream. */
+int32_t pkv_varlen_num_splits(const pkv_varlen_args* a);
+size_t pkv_varlen_workspace_size(const pkv_varlen_args* a);
+
+pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream);
+
+/* ----------------------------------------------------------------------- merge
+ * Merge two attention states of the same queries (cascade attention: a state
+ * over the shared prefix and one over each request's own suffix):
+ *   lse = log(exp(prefix_lse) + exp(suffix_lse))
+ *   out = exp(prefix_lse - lse) * prefix_out + exp(suffix_lse - lse) * suffix_out
+ * computed in fp32 with the larger lse subtracted first. A state whose lse is
+ * -inf has weight 0; if both are -inf, out = 0 and lse = -inf.
+ * Layouts: out, prefix_out, suffix_out [num_tokens, num_heads, head_size] in
+ * dtype (BF16 or F32); prefix_lse, suffix_lse, out_lse [num_heads, num_tokens]
+ * fp32; out_lse may be NULL. out may alias prefix_out or suffix_out.          */
+pkv_status pkv_merge_attn_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,
+                                 const void* suffix_out, const float* suffix_lse, int64_t num_tokens,
+                                 int32_t num_heads, int32_t head_size, pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------ utilities */
+
+/* Message for the last error on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t pkv_version(void);
+
+/* Kernel timing. When enabled, every pkv_varlen_fwd call records HIP events
+ * around its main attention kernel and around its split-merge kernel, on the
+ * call's stream (at most 4096 calls are kept; later ones are not recorded).
+ * pkv_timing_collect waits for the recorded events, returns the number of
+ * calls and the summed milliseconds of each kernel, and clears the record.
+ * Enabling creates the events (it is the only call that allocates); disabling
+ * releases them. Not thread-safe.                                            */
+pkv_status pkv_timing_enable(int32_t on);
+pkv_status pkv_timing_collect(int32_t* calls, double* main_ms, double* merge_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKVFLASH_H */

@@ -70,6 +70,8 @@ def lib():
         L.or_attention_split.argtypes = common + [i64, vp, vp]
         L.or_merge.restype = None
         L.or_merge.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, vp]
+        L.or_encode_e4m3fn_array.restype = None
+        L.or_encode_e4m3fn_array.argtypes = [vp, i64, flt, vp]
         L.or_num_threads.restype = i32
         L.or_num_threads.argtypes = []
         _lib = L
@@ -210,6 +212,14 @@ def decode_e4m3fn(code: int) -> float:
 
 def encode_e4m3fn(y: float) -> int:
     return int(lib().or_encode_e4m3fn(float(y)))
+
+
+def encode_e4m3fn_array(x: np.ndarray, scale: float = 1.0) -> np.ndarray:
+    """Vectorised encode of binary32 values (after division by ``scale``)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().or_encode_e4m3fn_array(_ptr(x), x.size, float(scale), _ptr(out))
+    return out
 
 
 def encode_bf16(x: float) -> int:

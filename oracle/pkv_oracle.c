@@ -531,3 +531,14 @@ void or_merge(const double* o1, const double* lse1, const double* o2, const doub
         }
     }
 }
+
+/* Encode n binary32 values: out[i] = or_encode_e4m3fn(fl32(x[i] / scale)).
+ * Used to check an encoder exhaustively over all 2^32 inputs. */
+void or_encode_e4m3fn_array(const float* x, int64_t n, float scale, uint8_t* out) {
+    e4m3_table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        volatile float y = x[i] / scale;
+        out[i] = or_encode_e4m3fn(y);
+    }
+}

@@ -1,0 +1,352 @@
+// pkv_api.cpp -- host side of the C ABI declared in include/pkvflash.h:
+// argument validation, the choice of kernel and of the KV split, launches on
+// the caller's stream, error reporting and optional kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/pkvflash.h"
+#include "pkv_kernels.h"
+
+using namespace pkv;
+
+namespace {
+
+thread_local std::string g_err;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+pkv_status ok() {
+    g_err.clear();
+    return PKV_OK;
+}
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+    return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+enum class Kind { Decode, Prefill, Generic };
+
+struct Plan {
+    Kind kind;
+    int32_t splits;
+    int32_t split_len;
+    int32_t n_qtiles;
+    size_t workspace;  // bytes needed for `splits`
+};
+
+bool mfma_head(int hd) { return hd == 64 || hd == 128 || hd == 256; }
+
+// Sizes, types and their consistency (no pointer checks).
+pkv_status validate_sizes(const pkv_varlen_args* a);
+
+// Everything pkv_varlen_fwd needs: sizes plus the required pointers.
+pkv_status validate(const pkv_varlen_args* a) {
+    pkv_status st = validate_sizes(a);
+    if (st != PKV_OK || a->num_tokens == 0) return st;
+    if (!a->q || !a->k_cache || !a->v_cache || !a->out || !a->query_start_loc)
+        return fail(PKV_ERR_INVALID_ARG, "q, k_cache, v_cache, out and query_start_loc must be non-NULL");
+    if (a->block_table && !a->seq_lens) return fail(PKV_ERR_INVALID_ARG, "a paged cache needs seq_lens");
+    if (a->kv_dtype == PKV_FP8_E4M3FN && (!a->k_scale || !a->v_scale))
+        return fail(PKV_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    return ok();
+}
+
+pkv_status validate_sizes(const pkv_varlen_args* a) {
+    if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+    if (a->num_tokens < 0 || a->num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "negative num_tokens or num_seqs");
+    if (a->num_tokens >= (int64_t(1) << 31)) return fail(PKV_ERR_UNSUPPORTED, "num_tokens must be < 2^31");
+    if (a->num_tokens > 0 && a->num_seqs == 0) return fail(PKV_ERR_INVALID_ARG, "tokens without sequences");
+    if (a->num_heads <= 0 || a->num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_heads and num_kv_heads must be positive");
+    if (a->num_heads % a->num_kv_heads != 0)
+        return fail(PKV_ERR_INVALID_ARG, "num_heads (%d) is not a multiple of num_kv_heads (%d)", a->num_heads, a->num_kv_heads);
+    if (a->num_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_heads must be <= 65535");
+    if (a->head_size <= 0 || a->head_size % 8 != 0 || a->head_size > 256)
+        return fail(PKV_ERR_UNSUPPORTED, "head_size %d: must be a multiple of 8 and at most 256", a->head_size);
+    const bool ok_types = (a->q_dtype == PKV_BF16 && (a->kv_dtype == PKV_BF16 || a->kv_dtype == PKV_FP8_E4M3FN)) ||
+                          (a->q_dtype == PKV_F32 && a->kv_dtype == PKV_F32);
+    if (!ok_types) return fail(PKV_ERR_UNSUPPORTED, "unsupported (q_dtype, kv_dtype) = (%d, %d)", a->q_dtype, a->kv_dtype);
+    if (!std::isfinite(a->softmax_scale)) return fail(PKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (a->num_splits < 0 || a->num_splits > 256) return fail(PKV_ERR_INVALID_ARG, "num_splits must be in [0, 256]");
+    if (a->num_tokens == 0) return ok();
+    if (a->num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_seqs must be <= 65535");
+    if (a->max_seqlen_q <= 0) return fail(PKV_ERR_INVALID_ARG, "max_seqlen_q must be positive");
+    if (a->num_tokens > (int64_t)a->num_seqs * a->max_seqlen_q)
+        return fail(PKV_ERR_INVALID_ARG, "num_tokens exceeds num_seqs * max_seqlen_q");
+    if (a->block_table) {
+        if (a->block_size <= 0) return fail(PKV_ERR_INVALID_ARG, "block_size must be positive");
+        if (a->num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
+        if (a->num_blocks * (int64_t)a->block_size >= (int64_t(1) << 31))
+            return fail(PKV_ERR_UNSUPPORTED, "num_blocks * block_size must be < 2^31");
+        if (a->max_seqlen_k < a->max_seqlen_q)
+            return fail(PKV_ERR_INVALID_ARG, "max_seqlen_k (%d) < max_seqlen_q (%d): seq_lens include the new tokens",
+                        a->max_seqlen_k, a->max_seqlen_q);
+        if (a->block_table_stride < cdiv(a->max_seqlen_k, a->block_size))
+            return fail(PKV_ERR_INVALID_ARG, "block_table_stride %lld < ceil(max_seqlen_k / block_size) = %lld",
+                        (long long)a->block_table_stride, (long long)cdiv(a->max_seqlen_k, a->block_size));
+    }
+    return ok();
+}
+
+Plan make_plan(const pkv_varlen_args* a) {
+    Plan pl{};
+    const int g = a->num_heads / a->num_kv_heads;
+    const bool paged = a->block_table != nullptr;
+    const int64_t max_k = paged ? a->max_seqlen_k : a->max_seqlen_q;
+    const bool mfma = a->q_dtype == PKV_BF16 && mfma_head(a->head_size) && g <= kPrefillRows;
+    int64_t items;
+    int align;
+    if (mfma && (int64_t)a->max_seqlen_q * g <= kDecodeRows) {
+        pl.kind = Kind::Decode;
+        items = (int64_t)a->num_seqs * a->num_kv_heads;
+        align = kDecodeTile * kDecodeWaves;
+    } else if (mfma) {
+        pl.kind = Kind::Prefill;
+        const int tpw = kPrefillRows / g;
+        pl.n_qtiles = (int32_t)cdiv(a->max_seqlen_q, tpw);
+        items = (int64_t)a->num_seqs * a->num_kv_heads * pl.n_qtiles;
+        align = kPrefillTile * 4;
+    } else {
+        pl.kind = Kind::Generic;
+        items = a->num_tokens * a->num_heads;
+        align = 64;
+    }
+    int64_t S = 1;
+    if (a->num_splits > 1) {
+        S = a->num_splits;
+    } else if (a->num_splits == 0 && pl.kind != Kind::Generic) {
+        // Enough workgroups to fill 256 CUs several times over, but at least
+        // 512 keys of work per split.
+        const int64_t by_len = cdiv(max_k, 512);
+        if (items < 2048) S = std::min<int64_t>(by_len, std::max<int64_t>(1, cdiv(4096, items)));
+        S = std::max<int64_t>(1, std::min<int64_t>(S, 64));
+    }
+    if (S > 1) {
+        int64_t len = cdiv(cdiv(max_k, S), align) * align;
+        if (len <= 0) len = align;
+        S = cdiv(max_k, len);
+        pl.split_len = (int32_t)len;
+    }
+    if (S <= 1) {
+        S = 1;
+        pl.split_len = (int32_t)std::max<int64_t>(max_k, 1);
+    }
+    pl.splits = (int32_t)S;
+    pl.workspace = S > 1 ? (size_t)S * a->num_tokens * a->num_heads * (a->head_size + 1) * sizeof(float) : 0;
+    return pl;
+}
+
+// ------------------------------------------------------------------ timing
+
+struct Timing {
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // 4 per call: main start/end, merge start/end
+    std::vector<char> has_merge;
+    int calls = 0;
+};
+Timing g_tim;
+constexpr int kTimingCap = 4096;
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_varlen_args_size(void) { return sizeof(pkv_varlen_args); }
+
+pkv_status pkv_varlen_check(const pkv_varlen_args* a) { return validate(a); }
+
+int32_t pkv_varlen_num_splits(const pkv_varlen_args* a) {
+    if (validate_sizes(a) != PKV_OK) return 0;
+    return make_plan(a).splits;
+}
+
+size_t pkv_varlen_workspace_size(const pkv_varlen_args* a) {
+    if (validate_sizes(a) != PKV_OK) return 0;
+    return make_plan(a).workspace;
+}
+
+pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
+    pkv_status st = validate(a);
+    if (st != PKV_OK || a->num_tokens == 0) return st;
+    Plan pl = make_plan(a);
+    if (pl.splits > 1 && (a->workspace == nullptr || a->workspace_bytes < pl.workspace)) {
+        if (a->num_splits > 1)
+            return fail(PKV_ERR_WORKSPACE, "num_splits=%d needs %zu workspace bytes, got %zu", pl.splits, pl.workspace,
+                        a->workspace ? a->workspace_bytes : (size_t)0);
+        // automatic choice without room for partials: run unsplit
+        pl.splits = 1;
+        pl.split_len = (int32_t)std::max<int64_t>(a->block_table ? a->max_seqlen_k : a->max_seqlen_q, 1);
+        pl.workspace = 0;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    FwdParams p{};
+    p.q = a->q;
+    p.k_cache = a->k_cache;
+    p.v_cache = a->v_cache;
+    p.out = a->out;
+    p.lse = a->lse;
+    p.qsl = a->query_start_loc;
+    p.seq_lens = a->block_table ? a->seq_lens : nullptr;
+    p.bt = a->block_table;
+    p.k_scale = a->k_scale;
+    p.v_scale = a->v_scale;
+    p.bt_stride = a->block_table_stride;
+    p.T = a->num_tokens;
+    p.B = a->num_seqs;
+    p.H = a->num_heads;
+    p.Hkv = a->num_kv_heads;
+    p.g = a->num_heads / a->num_kv_heads;
+    p.hd = a->head_size;
+    p.bs = a->block_table ? a->block_size : 1;
+    p.num_splits = pl.splits;
+    p.split_len = pl.split_len;
+    p.n_qtiles = pl.n_qtiles;
+    p.causal = a->causal ? 1 : 0;
+    p.scale_log2 = a->softmax_scale * 1.4426950408889634f;  // log2(e): kernels use exp2
+    if (pl.splits > 1) {
+        p.part_o = (float*)a->workspace;
+        p.part_lse = p.part_o + (size_t)pl.splits * a->num_tokens * a->num_heads * a->head_size;
+    }
+    const KvType kv = a->kv_dtype == PKV_FP8_E4M3FN ? KvType::FP8 : a->kv_dtype == PKV_F32 ? KvType::F32 : KvType::BF16;
+
+    const bool timed = g_tim.on && g_tim.calls < kTimingCap;
+    hipEvent_t* ev = timed ? &g_tim.ev[4 * g_tim.calls] : nullptr;
+    if (timed) {
+        hipError_t e = hipEventRecord(ev[0], s);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    hipError_t e;
+    switch (pl.kind) {
+        case Kind::Decode: e = launch_decode(p, kv, s); break;
+        case Kind::Prefill: e = launch_prefill(p, kv, s); break;
+        default: e = launch_generic(p, kv, a->q_dtype == PKV_F32, s); break;
+    }
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    if (timed) {
+        e = hipEventRecord(ev[1], s);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    if (pl.splits > 1) {
+        if (timed) (void)hipEventRecord(ev[2], s);
+        e = launch_combine(p, a->q_dtype == PKV_F32, s);
+        if (e != hipSuccess) return hip_fail(e, "split merge kernel launch");
+        if (timed) (void)hipEventRecord(ev[3], s);
+    }
+    if (timed) {
+        g_tim.has_merge[g_tim.calls] = pl.splits > 1;
+        ++g_tim.calls;
+    }
+    return ok();
+}
+
+pkv_status pkv_cache_write(const void* key, const void* value, pkv_dtype src_dtype, void* k_cache, void* v_cache,
+                           pkv_dtype cache_dtype, const int64_t* slot_mapping, int64_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size, int64_t num_blocks,
+                           const float* k_scale, const float* v_scale, void* stream) {
+    if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_kv_heads <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_INVALID_ARG, "num_kv_heads, block_size and num_blocks must be positive");
+    if (head_size <= 0 || head_size % 8 != 0 || head_size > 256)
+        return fail(PKV_ERR_UNSUPPORTED, "head_size %d: must be a multiple of 8 and at most 256", head_size);
+    int kind;
+    if (src_dtype == cache_dtype && (src_dtype == PKV_F32 || src_dtype == PKV_BF16)) kind = 0;
+    else if (src_dtype == PKV_F32 && cache_dtype == PKV_BF16) kind = 1;
+    else if ((src_dtype == PKV_F32 || src_dtype == PKV_BF16) && cache_dtype == PKV_FP8_E4M3FN) kind = 2;
+    else return fail(PKV_ERR_UNSUPPORTED, "unsupported (src_dtype, cache_dtype) = (%d, %d)", src_dtype, cache_dtype);
+    if (kind == 2 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    if (num_tokens == 0) return ok();
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+        return fail(PKV_ERR_INVALID_ARG, "key, value, k_cache, v_cache and slot_mapping must be non-NULL");
+    if (2 * num_tokens * ((int64_t)num_kv_heads * head_size / 8) >= (int64_t(1) << 31) * 256)
+        return fail(PKV_ERR_UNSUPPORTED, "too many tokens for one launch");
+    hipError_t e = launch_cache_write(key, value, src_dtype == PKV_F32, k_cache, v_cache, kind, slot_mapping,
+                                      num_tokens, num_kv_heads, head_size, k_scale, v_scale, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "cache write launch");
+    return ok();
+}
+
+pkv_status pkv_merge_attn_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,
+                                 const void* suffix_out, const float* suffix_lse, int64_t num_tokens,
+                                 int32_t num_heads, int32_t head_size, pkv_dtype dtype, void* stream) {
+    if (num_tokens < 0 || num_heads <= 0 || head_size <= 0)
+        return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0, num_heads and head_size positive");
+    if (head_size % 8 != 0 || head_size > 256)
+        return fail(PKV_ERR_UNSUPPORTED, "head_size %d: must be a multiple of 8 and at most 256", head_size);
+    if (dtype != PKV_BF16 && dtype != PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "merge supports BF16 and F32 states");
+    if (num_tokens == 0) return ok();
+    if (!out || !prefix_out || !prefix_lse || !suffix_out || !suffix_lse)
+        return fail(PKV_ERR_INVALID_ARG, "out, prefix_out, prefix_lse, suffix_out and suffix_lse must be non-NULL");
+    if (num_tokens * num_heads * (head_size / 4) >= (int64_t(1) << 31) * 256)
+        return fail(PKV_ERR_UNSUPPORTED, "too many rows for one launch");
+    hipError_t e = launch_merge(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse, num_tokens, num_heads,
+                                head_size, dtype == PKV_F32, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return ok();
+}
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+int32_t pkv_version(void) { return 100; }
+
+pkv_status pkv_timing_enable(int32_t on) {
+    if (on && !g_tim.on) {
+        g_tim.ev.assign(4 * kTimingCap, nullptr);
+        g_tim.has_merge.assign(kTimingCap, 0);
+        for (auto& e : g_tim.ev) {
+            hipError_t r = hipEventCreate(&e);
+            if (r != hipSuccess) return hip_fail(r, "hipEventCreate");
+        }
+        g_tim.calls = 0;
+        g_tim.on = true;
+    } else if (!on && g_tim.on) {
+        for (auto& e : g_tim.ev)
+            if (e) (void)hipEventDestroy(e);
+        g_tim.ev.clear();
+        g_tim.has_merge.clear();
+        g_tim.calls = 0;
+        g_tim.on = false;
+    }
+    return ok();
+}
+
+pkv_status pkv_timing_collect(int32_t* calls, double* main_ms, double* merge_ms) {
+    double a = 0, b = 0;
+    for (int i = 0; i < g_tim.calls; ++i) {
+        hipError_t e = hipEventSynchronize(g_tim.ev[4 * i + 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float ms = 0;
+        e = hipEventElapsedTime(&ms, g_tim.ev[4 * i], g_tim.ev[4 * i + 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        a += ms;
+        if (g_tim.has_merge[i]) {
+            e = hipEventSynchronize(g_tim.ev[4 * i + 3]);
+            if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+            e = hipEventElapsedTime(&ms, g_tim.ev[4 * i + 2], g_tim.ev[4 * i + 3]);
+            if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+            b += ms;
+        }
+    }
+    if (calls) *calls = g_tim.calls;
+    if (main_ms) *main_ms = a;
+    if (merge_ms) *merge_ms = b;
+    g_tim.calls = 0;
+    return ok();
+}
+
+}  // extern "C"

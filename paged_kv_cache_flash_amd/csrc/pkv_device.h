@@ -1,0 +1,93 @@
+// pkv_device.h -- device-side building blocks for the gfx950 attention kernels.
+//
+// Lane layouts (verified on gfx950 with an in-bounds probe of each builtin):
+//  v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8*(l/16)+e], B[8*(l/16)+e][l%16]
+//      (e = 0..7) and C[4*(l/16)+i][l%16] (i = 0..3).
+//  v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8*(l/32)+e], B[8*(l/32)+e][l%32]
+//      and C[8*(i/4) + 4*(l/32) + i%4][l%32] (i = 0..15).
+//  ds_read_b64_tr_b16: inside each group of 16 lanes, output lane i, element e is
+//      element i%4 of the 8-byte chunk addressed by lane 4e + i/4 of the group;
+//      i.e. lanes 4e..4e+3 address row e of a 4 x 16 block and lane i receives
+//      column i.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+// Transposed 4 x b16 read from LDS (see the layout note at the top).
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Four e4m3fn bytes (one dword) -> four bf16 packed in two dwords. Exact:
+// every e4m3fn value is representable in bf16.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    u32x2 r;
+    r.x = pack_bf16x2(a.x, a.y);
+    r.y = pack_bf16x2(b.x, b.y);
+    return r;
+}
+
+// Eight e4m3fn bytes -> eight bf16 (one 16-byte MFMA operand).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 w) {
+    u32x2 a = fp8x4_to_bf16x4(w.x), b = fp8x4_to_bf16x4(w.y);
+    return u32x4{a.x, a.y, b.x, b.y};
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Keep LDS traffic of one wave in program order and visible to its own later
+// reads: wait for outstanding LDS operations and stop the compiler moving
+// memory operations across this point.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Physical cache row (block * block_size + offset) of logical key `pos`
+// (the host guarantees num_blocks * block_size < 2^31).
+// block_table == nullptr means the flat layout: row = flat_base + pos.
+__device__ __forceinline__ int32_t kv_row(const int32_t* __restrict__ bt_row, int32_t pos, int32_t bs,
+                                          int32_t flat_base) {
+    if (bt_row == nullptr) return flat_base + pos;
+    int32_t blk = pos / bs;
+    int32_t off = pos - blk * bs;
+    return bt_row[blk] * bs + off;
+}
+
+}  // namespace pkv

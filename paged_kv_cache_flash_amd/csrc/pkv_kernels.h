@@ -1,0 +1,56 @@
+// pkv_kernels.h -- internal interface between the host API and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Everything a forward kernel needs, passed by value as the kernel argument.
+struct FwdParams {
+    const void* q;            // [T, H, hd] (bf16 or f32)
+    const void* k_cache;      // paged [num_blocks, bs, Hkv, hd] or flat [T, Hkv, hd]
+    const void* v_cache;
+    void* out;                // [T, H, hd], type of q
+    float* lse;               // [H, T] or nullptr
+    float* part_o;            // split partials [S, T, H, hd] fp32 (S > 1)
+    float* part_lse;          // [S, H, T] fp32
+    const int32_t* qsl;       // [B+1]
+    const int32_t* seq_lens;  // [B] or nullptr (flat)
+    const int32_t* bt;        // block table or nullptr (flat)
+    const float* k_scale;     // fp8 only
+    const float* v_scale;
+    int64_t bt_stride;
+    int64_t T;
+    int32_t B, H, Hkv, g, hd, bs;
+    int32_t num_splits;       // >= 1
+    int32_t split_len;        // keys per split (multiple of the key tile) when num_splits > 1
+    int32_t n_qtiles;         // prefill: query tiles per (request, kv head)
+    int32_t causal;
+    float scale_log2;         // softmax_scale * log2(e)
+};
+
+enum class KvType { BF16, FP8, F32 };
+
+// Launchers return hipSuccess or the launch error.
+hipError_t launch_decode(const FwdParams& p, KvType kv, hipStream_t s);
+hipError_t launch_prefill(const FwdParams& p, KvType kv, hipStream_t s);
+hipError_t launch_generic(const FwdParams& p, KvType kv, bool q_f32, hipStream_t s);
+hipError_t launch_combine(const FwdParams& p, bool out_f32, hipStream_t s);
+hipError_t launch_merge(void* out, float* out_lse, const void* po, const float* plse, const void* so,
+                        const float* slse, int64_t T, int32_t H, int32_t hd, bool f32, hipStream_t s);
+hipError_t launch_cache_write(const void* key, const void* value, int src_f32, void* kc, void* vc, int cache_kind,
+                              const int64_t* slots, int64_t T, int32_t Hkv, int32_t hd, const float* ks,
+                              const float* vs, hipStream_t s);
+
+// Decode kernel geometry: rows (q tokens x heads of a group) per work item,
+// keys per tile, waves per workgroup.
+constexpr int kDecodeRows = 16;
+constexpr int kDecodeTile = 32;
+constexpr int kDecodeWaves = 4;
+// Prefill kernel geometry.
+constexpr int kPrefillRowsPerWave = 32;
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = kPrefillRowsPerWave * kPrefillWaves;
+constexpr int kPrefillTile = 32;
+
+}  // namespace pkv

@@ -1,0 +1,127 @@
+"""Helpers for GPU tests: move seeded problems to the device, run the library
+through its Python binding, and compute the oracle's answer on the host.
+The oracle always works from the host-side inputs and its own cache write;
+nothing computed on the GPU is fed to it."""
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_flash_amd as pkv
+
+DEV = torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    if a.dtype == np.uint8:
+        return torch.from_numpy(a).to(DEV).view(torch.float8_e4m3fn)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
+    return t.cpu().numpy()
+
+
+def out_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+class GpuProblem:
+    """A workloads.Problem resident on the GPU, its cache filled by pkv_cache_write."""
+
+    def __init__(self, prob, write_new_separately: bool = False):
+        self.prob = prob
+        self.q = to_dev(prob.q)
+        self.qsl = to_dev(prob.query_start_loc)
+        self.k_scale = self.v_scale = None
+        if prob.cache_dtype == "fp8":
+            self.k_scale = torch.tensor([prob.k_scale], dtype=torch.float32, device=DEV)
+            self.v_scale = torch.tensor([prob.v_scale], dtype=torch.float32, device=DEV)
+        if prob.paged:
+            kc, vc = prob.empty_cache()
+            self.kc, self.vc = to_dev(kc), to_dev(vc)
+            self.seq_lens = to_dev(prob.seq_lens)
+            self.bt = to_dev(prob.block_table)
+            if write_new_separately:
+                ctx_rows = prob.context_rows()
+                self.write(ctx_rows)
+                self.write(prob.new_rows)
+            else:
+                self.write(np.arange(len(prob.kv_src_k)))
+        else:
+            rows = np.concatenate(prob.pos_rows)
+            self.kc, self.vc = to_dev(prob.kv_src_k[rows]), to_dev(prob.kv_src_v[rows])
+            self.seq_lens = None
+            self.bt = None
+
+    def write(self, rows):
+        p = self.prob
+        if len(rows) == 0:
+            return
+        pkv.pkv_cache_write(to_dev(p.kv_src_k[rows]), to_dev(p.kv_src_v[rows]), self.kc, self.vc,
+                            to_dev(p.kv_slots[rows]), self.k_scale, self.v_scale)
+
+    def run(self, num_splits=0, causal=None, block_table=None):
+        p = self.prob
+        bt = self.bt if block_table is None else block_table
+        return pkv.pkv_varlen_fwd(self.q, self.kc, self.vc, self.qsl, self.seq_lens, bt, p.max_seqlen_q,
+                                  p.max_seqlen_k if p.paged else p.max_seqlen_q, p.scale,
+                                  causal=p.causal if causal is None else causal, k_scale=self.k_scale,
+                                  v_scale=self.v_scale, num_splits=num_splits, return_lse=True)
+
+
+def oracle_cache(prob):
+    kc, vc = prob.empty_cache()
+    return oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc, vc, prob.kv_slots, prob.bs,
+                              k_scale=prob.k_scale, v_scale=prob.v_scale)
+
+
+def oracle_attention(prob, rows=None, causal=None, caches=None):
+    causal = prob.causal if causal is None else causal
+    if not prob.paged:
+        flat = np.concatenate(prob.pos_rows)
+        return oracle.attention(prob.q, prob.kv_src_k[flat], prob.kv_src_v[flat], prob.query_start_loc,
+                                scale=prob.scale, causal=causal, rows=rows)
+    kc, vc = caches if caches is not None else oracle_cache(prob)
+    return oracle.attention(prob.q, kc, vc, prob.query_start_loc, prob.seq_lens, prob.block_table,
+                            scale=prob.scale, causal=causal, rows=rows, k_scale=prob.k_scale,
+                            v_scale=prob.v_scale)
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at |x| (8 significant bits): the rounding error of
+    storing x as bf16. Zero where x == 0."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - 8), 0.0)
+
+
+def assert_parity(out, lse, ref, ref_lse, out_tol, lse_tol, rows=None, what=""):
+    """Max abs error <= out_tol per output element; for a bf16 output the bar
+    is widened by half a bf16 ulp of the oracle value, the error of rounding
+    the exact answer itself to bf16 (it matters only for |out| >= 4, where that
+    rounding alone can exceed 1e-2)."""
+    o = out_f64(out)
+    l_ = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        o = o[rows]
+        l_ = l_[:, rows]
+    assert o.shape == ref.shape
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    err = np.abs(o - ref)
+    allowed = out_tol + (bf16_half_ulp(ref) if out.dtype == torch.bfloat16 else 0.0)
+    i = np.unravel_index(np.argmax(err - allowed), err.shape)
+    assert np.all(err <= allowed), (f"{what}: |out-oracle| = {err[i]:.3e} > {allowed if np.isscalar(allowed) else allowed[i]:.3e}"
+                                    f" at {i} (|o|={abs(ref[i]):.3f}); max abs error {err.max():.3e}")
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(l_), fin), f"{what}: lse finiteness differs"
+    if fin.any():
+        lerr = np.abs(l_[fin] - ref_lse[fin]).max()
+        assert lerr <= lse_tol, f"{what}: max|lse-oracle| = {lerr:.3e}"

@@ -1,0 +1,162 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every entry point include/pkvflash.h declares, the Python mirror of the args
+struct matches, and host validation returns the documented error classes.
+Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_flash_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkvflash.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = pkv.lib()
+    names = declared_functions()
+    assert "pkv_varlen_fwd" in names and "pkv_cache_write" in names and "pkv_merge_attn_states" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(pkv.EXPORTS)
+
+
+def test_struct_mirror_size():
+    assert pkv.lib().pkv_varlen_args_size() == ctypes.sizeof(pkv.pkv_varlen_args)
+
+
+def test_version():
+    assert pkv.lib().pkv_version() >= 100
+
+
+FAKE = 0x1000  # never dereferenced: validation is host-only
+
+
+def good_args(**kw):
+    a = pkv.pkv_varlen_args()
+    a.q = a.k_cache = a.v_cache = a.out = a.query_start_loc = a.seq_lens = a.block_table = FAKE
+    a.num_tokens, a.num_seqs, a.num_heads, a.num_kv_heads, a.head_size = 64, 64, 32, 8, 128
+    a.block_size, a.num_blocks, a.block_table_stride = 16, 10000, 256
+    a.max_seqlen_q, a.max_seqlen_k = 1, 4096
+    a.q_dtype, a.kv_dtype, a.softmax_scale, a.causal = pkv.PKV_BF16, pkv.PKV_BF16, 0.088, 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def check(a):
+    return pkv.lib().pkv_varlen_check(ctypes.byref(a))
+
+
+def test_valid_args_pass():
+    assert check(good_args()) == pkv.PKV_OK
+    assert check(good_args(kv_dtype=pkv.PKV_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE)) == pkv.PKV_OK
+    assert check(good_args(q_dtype=pkv.PKV_F32, kv_dtype=pkv.PKV_F32, head_size=16)) == pkv.PKV_OK
+    assert check(good_args(block_table=None, seq_lens=None, max_seqlen_q=8)) == pkv.PKV_OK
+    assert check(good_args(num_tokens=0, q=None)) == pkv.PKV_OK  # empty batch is a no-op
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_heads=30), pkv.PKV_ERR_INVALID_ARG),          # H % Hkv != 0
+    (dict(num_kv_heads=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(head_size=100), pkv.PKV_ERR_UNSUPPORTED),        # not a multiple of 8
+    (dict(head_size=264), pkv.PKV_ERR_UNSUPPORTED),        # > 256
+    (dict(block_size=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(num_blocks=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(num_blocks=1 << 28, block_size=16), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(q=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(out=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(seq_lens=None), pkv.PKV_ERR_INVALID_ARG),        # paged without seq_lens
+    (dict(max_seqlen_q=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(max_seqlen_k=0, max_seqlen_q=1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(block_table_stride=10), pkv.PKV_ERR_INVALID_ARG),  # table too narrow for max_seqlen_k
+    (dict(num_tokens=100, num_seqs=64, max_seqlen_q=1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(kv_dtype=pkv.PKV_FP8_E4M3FN), pkv.PKV_ERR_INVALID_ARG),  # fp8 without scales
+    (dict(q_dtype=pkv.PKV_F32), pkv.PKV_ERR_UNSUPPORTED),  # f32 q with bf16 cache
+    (dict(q_dtype=pkv.PKV_FP8_E4M3FN), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(num_splits=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(num_splits=300), pkv.PKV_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
+    (dict(num_tokens=-1), pkv.PKV_ERR_INVALID_ARG),
+])
+def test_invalid_args_rejected(kw, status):
+    a = good_args(**kw)
+    assert check(a) == status
+    assert pkv.lib().pkv_last_error().decode() != ""
+    # the forward rejects the same arguments before launching anything
+    assert pkv.lib().pkv_varlen_fwd(ctypes.byref(a), None) == status
+
+
+def test_null_args_pointer():
+    assert pkv.lib().pkv_varlen_check(None) == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_split_plan_and_workspace():
+    L = pkv.lib()
+    # long-context decode with few work items is split; the workspace holds
+    # fp32 partial outputs and lse per split
+    a = good_args(num_tokens=4, num_seqs=4, num_heads=64, num_kv_heads=8, max_seqlen_k=131072,
+                  block_size=256, block_table_stride=512, num_blocks=4096)
+    s = L.pkv_varlen_num_splits(ctypes.byref(a))
+    assert 16 <= s <= 64
+    assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == s * 4 * 64 * (128 + 1) * 4
+    a.num_splits = 1
+    assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 1
+    assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == 0
+    a.num_splits = 7
+    assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 7
+
+
+def test_forced_split_without_workspace_is_an_error():
+    a = good_args(num_splits=4)
+    assert pkv.lib().pkv_varlen_fwd(ctypes.byref(a), None) == pkv.PKV_ERR_WORKSPACE
+
+
+def test_cache_write_validation():
+    L = pkv.lib()
+    args = [FAKE, FAKE, pkv.PKV_BF16, FAKE, FAKE, pkv.PKV_BF16, FAKE, 8, 8, 128, 16, 100, None, None, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["key", "value", "src", "kc", "vc", "cache", "slots", "T", "Hkv", "hd", "bs", "nb", "ks", "vs", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.pkv_cache_write(*a)
+
+    assert call(T=0) == pkv.PKV_OK
+    assert call(T=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert call(hd=100) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(bs=0) == pkv.PKV_ERR_INVALID_ARG
+    assert call(src=pkv.PKV_BF16, cache=pkv.PKV_F32) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(src=pkv.PKV_FP8_E4M3FN, cache=pkv.PKV_FP8_E4M3FN) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(cache=pkv.PKV_FP8_E4M3FN) == pkv.PKV_ERR_INVALID_ARG  # fp8 without scales
+    assert call(slots=None) == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_merge_validation():
+    L = pkv.lib()
+    assert L.pkv_merge_attn_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, 4, 128, pkv.PKV_BF16, None) == pkv.PKV_OK
+    assert L.pkv_merge_attn_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 4, 100, pkv.PKV_BF16, None) == \
+        pkv.PKV_ERR_UNSUPPORTED
+    assert L.pkv_merge_attn_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 4, 128, pkv.PKV_FP8_E4M3FN, None) == \
+        pkv.PKV_ERR_UNSUPPORTED
+    assert L.pkv_merge_attn_states(None, None, FAKE, FAKE, FAKE, FAKE, 4, 4, 128, pkv.PKV_BF16, None) == \
+        pkv.PKV_ERR_INVALID_ARG
+
+
+def test_product_path_never_imports_the_oracle():
+    """The package and its sources must not reference the oracle."""
+    pkg = os.path.join(ROOT, "paged_kv_cache_flash_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "liboracle" not in text and "pkv_oracle" not in text, f
