@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+One step = one pass of the whole path over one synthetic batch: the cache
+write of this step's new tokens (pkv_cache_write), then the varlen attention
+forward over the paged cache (pkv_varlen_fwd: the attention kernel and, when
+the KV range is split, the log-sum-exp merge kernel). Inputs are resident in
+HBM before timing starts. The KV cache is replicated and the replicas are used
+in turn, so a step never finds its KV in the 256 MB last-level cache.
+
+Default workload (one GPU): paged decode, Llama-3-8B-like GQA (32 query / 8 kv
+heads, head size 128, bf16), batch 64, one query token per request, context
+lengths uniform in [512, 4096], page size 16, random block table. The metric is
+KV bytes read per second (GB/s) against the MI355X HBM peak of 8 TB/s.
+Other workloads (--workload): chunked_prefill (TFLOP/s against the 2.5 PFLOP/s
+bf16 dense MFMA peak), long_decode, long_decode_cascade, fp8_decode.
+
+Prints ONE JSON line. The float64 CPU oracle is timed on the same workload
+(rank 0, one GPU only) as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    "paged_decode": "paged decode, 32/8 heads GQA, head 128, bf16, batch 64, ctx U[512,4096], page 16",
+    "chunked_prefill": "chunked prefill, batch 8, new U[128,2048] on cached U[0,4096], 32/8 heads, head 128, "
+                       "bf16, page 16, causal",
+    "long_decode": "long-context split-KV decode, batch 4, ctx 131072, 64/8 heads, head 128, bf16, page 256",
+    "long_decode_cascade": "long decode as cascade: 4 requests share a 32768-token prefix, ctx 131072, "
+                           "64/8 heads, head 128, bf16, page 256",
+    "fp8_decode": "decode over an fp8 e4m3fn cache, bf16 q, batch 128, ctx U[1024,8192], 32/8 heads, head 128",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make(name, bs):
+    import workloads
+    if name == "paged_decode":
+        return workloads.paged_decode()
+    if name == "chunked_prefill":
+        return workloads.chunked_prefill()
+    if name == "long_decode":
+        return workloads.long_decode()
+    if name == "long_decode_cascade":
+        return workloads.long_decode(shared_prefix=32768)
+    if name == "fp8_decode":
+        return workloads.fp8_decode(bs=bs or 16)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def kv_elem_bytes(prob):
+    return 1 if prob.cache_dtype == "fp8" else 2
+
+
+def kv_bytes(prob, unique=False):
+    """Algorithmic KV bytes of one forward: every request reads K and V of all
+    its seq_len positions (cascade: the shared prefix once)."""
+    per_tok = prob.Hkv * prob.hd * 2 * kv_elem_bytes(prob)
+    toks = int(prob.seq_lens.sum())
+    if unique and prob.shared_prefix:
+        toks -= (prob.B - 1) * prob.shared_prefix
+    return toks * per_tok
+
+
+def visible_flops(prob):
+    """4 * hd * H * (visible query-key pairs): QK^T and PV, causal pairs only."""
+    ql = prob.q_lens.astype(np.int64)
+    ctx = prob.ctx_lens.astype(np.int64)
+    pairs = int((ql * ctx + ql * (ql + 1) // 2).sum()) if prob.causal else int((ql * prob.seq_lens).sum())
+    return 4 * prob.hd * prob.H * pairs
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="paged_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--block-size", type=int, default=0, help="page size for fp8_decode (1, 8, 16, 64, 256)")
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--replicas", type=int, default=0, help="KV cache copies used in turn (0 = enough for 1.5 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the attention shards by request "
+              "or kv head with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_flash_amd as pkv
+
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        if a.dtype == np.uint8:
+            return torch.from_numpy(a).to(dev).view(torch.float8_e4m3fn)
+        return torch.from_numpy(a).to(dev)
+    t0 = time.time()
+    prob = make(args.workload, args.block_size)
+    log(f"[bench] workload {args.workload}: B={prob.B} T={prob.T} sumL={int(prob.seq_lens.sum())} "
+        f"H={prob.H} Hkv={prob.Hkv} hd={prob.hd} bs={prob.bs} cache={prob.cache_dtype} "
+        f"(generated in {time.time() - t0:.1f}s)")
+
+    # device inputs
+    q = to_dev(prob.q)
+    qsl = to_dev(prob.query_start_loc)
+    seq_lens = to_dev(prob.seq_lens)
+    bt = to_dev(prob.block_table)
+    ks = vs = None
+    if prob.cache_dtype == "fp8":
+        ks = torch.tensor([prob.k_scale], dtype=torch.float32, device=dev)
+        vs = torch.tensor([prob.v_scale], dtype=torch.float32, device=dev)
+    new_rows = prob.new_rows
+    k_new, v_new, slots_new = to_dev(prob.kv_src_k[new_rows]), to_dev(prob.kv_src_v[new_rows]), \
+        to_dev(prob.kv_slots[new_rows])
+    cache_bytes = 2 * prob.num_blocks * prob.bs * prob.Hkv * prob.hd * kv_elem_bytes(prob)
+    R = args.replicas or max(1, min(8, int(np.ceil(1.5e9 / cache_bytes)) + 1))
+    ctx_rows = prob.context_rows()
+    reps = []
+    kc0, vc0 = prob.empty_cache()
+    for _ in range(R):
+        kc, vc = to_dev(kc0), to_dev(vc0)
+        for c0 in range(0, len(ctx_rows), 1 << 20):
+            rr = ctx_rows[c0:c0 + (1 << 20)]
+            pkv.pkv_cache_write(to_dev(prob.kv_src_k[rr]), to_dev(prob.kv_src_v[rr]), kc, vc,
+                                to_dev(prob.kv_slots[rr]), ks, vs)
+        reps.append((kc, vc))
+    del kc0, vc0
+    torch.cuda.synchronize()
+    log(f"[bench] {R} cache replicas of {cache_bytes / 1e9:.3f} GB resident")
+
+    out = torch.empty_like(q)
+    lse = torch.empty((prob.H, prob.T), dtype=torch.float32, device=dev)
+    cascade = prob.shared_prefix > 0
+    fwd_kw = dict(softmax_scale=prob.scale, causal=prob.causal, k_scale=ks, v_scale=vs)
+    if not cascade:
+        need = pkv.pkv_varlen_workspace_size(q, reps[0][0], reps[0][1], qsl, seq_lens, bt, prob.max_seqlen_q,
+                                             prob.max_seqlen_k, prob.scale, prob.causal, args.num_splits)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        splits = pkv.pkv_varlen_num_splits(q, reps[0][0], reps[0][1], qsl, seq_lens, bt, prob.max_seqlen_q,
+                                           prob.max_seqlen_k, prob.scale, prob.causal, args.num_splits)
+    else:
+        splits = None
+
+    def step(i):
+        kc, vc = reps[i % R]
+        pkv.pkv_cache_write(k_new, v_new, kc, vc, slots_new, ks, vs)
+        if cascade:
+            pkv.cascade_attention(q, kc, vc, qsl, seq_lens, bt, prob.shared_prefix, prob.max_seqlen_q,
+                                  prob.max_seqlen_k, prob.scale, k_scale=ks, v_scale=vs, out=out)
+        else:
+            pkv.pkv_varlen_fwd(q, kc, vc, qsl, seq_lens, bt, prob.max_seqlen_q, prob.max_seqlen_k, out=out,
+                               lse=lse, num_splits=args.num_splits, workspace=ws, **fwd_kw)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pkv.timing_enable(True)
+    pkv.timing_collect()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    calls, main_ms, merge_ms = pkv.timing_collect()
+    pkv.timing_enable(False)
+    ms_step = elapsed * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps in {elapsed:.4f}s: {ms_step:.4f} ms/step; attention calls {calls}, "
+        f"main kernel {main_ms / max(calls, 1):.4f} ms avg, merge {merge_ms / max(calls, 1):.4f} ms avg")
+
+    decode_like = args.workload != "chunked_prefill"
+    if decode_like:
+        kvb = kv_bytes(prob, unique=cascade)
+        value = kvb / (ms_step * 1e-3) / 1e9
+        metric, unit = "paged decode KV GB/s", "GB/s"
+        # the dominant kernel is the attention kernel; per step it reads the
+        # whole KV once (cascade: a prefix launch and a suffix launch per step)
+        achieved = kvb / (main_ms / args.steps * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        fl = visible_flops(prob)
+        value = fl / (ms_step * 1e-3) / 1e12
+        metric, unit = "causal prefill TFLOP/s", "TFLOP/s"
+        achieved = fl / (main_ms / args.steps * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # CPU-baseline leg: the float64 oracle (test infrastructure) on this
+        # workload. It first checks sampled rows of the timed output, then is
+        # timed on whole requests of the same batch.
+        # correctness spot check of the timed configuration against the oracle
+        import oracle
+        rng = np.random.default_rng(0)
+        sample = np.sort(rng.choice(prob.T, size=min(prob.T, 8), replace=False))
+        kc_o, vc_o = prob.empty_cache()
+        kc_o, vc_o = oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc_o, vc_o, prob.kv_slots, prob.bs,
+                                        k_scale=prob.k_scale, v_scale=prob.v_scale)
+        ref, ref_lse = oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, prob.seq_lens, prob.block_table,
+                                        scale=prob.scale, causal=prob.causal, rows=sample, k_scale=prob.k_scale,
+                                        v_scale=prob.v_scale)
+        tol = 5e-2 if prob.cache_dtype == "fp8" else 1e-2
+        o = out.float().cpu().numpy().astype(np.float64)[sample]
+        half_ulp = np.where(np.abs(ref) > 0, np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8), 0)
+        if not np.all(np.abs(o - ref) <= tol + half_ulp):
+            raise SystemExit(f"bench: sampled rows differ from the oracle by {np.abs(o - ref).max():.3e}")
+        if not cascade:
+            lerr = np.abs(lse.cpu().numpy()[:, sample] - ref_lse).max()
+            if lerr > 1e-3:
+                raise SystemExit(f"bench: sampled lse differs from the oracle by {lerr:.3e}")
+        log(f"[bench] sampled rows match the oracle (tolerance {tol})")
+        # the oracle as it stands, on whole requests of the same batch, until
+        # about --cpu-seconds of CPU work
+        nthr = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        # rows in packed order, a few at a time, until about --cpu-seconds
+        done_rows, done_bytes, done_flops, t_cpu = 0, 0, 0, 0.0
+        req_of = np.searchsorted(prob.query_start_loc, np.arange(prob.T), side="right") - 1
+        per_tok_kv = prob.Hkv * prob.hd * 2 * kv_elem_bytes(prob)
+        for r0 in range(0, prob.T, 16):
+            rows = np.arange(r0, min(prob.T, r0 + 16))
+            t1 = time.perf_counter()
+            oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, prob.seq_lens, prob.block_table,
+                             scale=prob.scale, causal=prob.causal, rows=rows, k_scale=prob.k_scale,
+                             v_scale=prob.v_scale, nthreads=nthr)
+            t_cpu += time.perf_counter() - t1
+            for tok in rows:
+                r = req_of[tok]
+                t_loc = tok - prob.query_start_loc[r]
+                n_vis = int(prob.ctx_lens[r]) + t_loc + 1 if prob.causal else int(prob.seq_lens[r])
+                done_flops += 4 * prob.hd * prob.H * n_vis
+                done_bytes += n_vis * per_tok_kv   # keys read for this row (all kv heads)
+            done_rows += len(rows)
+            if t_cpu >= args.cpu_seconds:
+                break
+        cpu_val = (done_bytes / t_cpu / 1e9) if decode_like else (done_flops / t_cpu / 1e12)
+        cpu = {"value": round(cpu_val, 4), "unit": unit, "cores": oracle.num_threads() if nthr <= 0 else nthr,
+               "kind": "oracle",
+               "sample": f"first {done_rows} of {prob.T} query rows of the same batch, all heads, float64, "
+                         f"{t_cpu:.1f}s"}
+        log(f"[bench] oracle: {cpu}")
+
+    cfg = {"workload": WORKLOADS[args.workload], "global_batch": prob.B, "seq_len": prob.max_seqlen_k,
+           "num_heads": prob.H, "num_kv_heads": prob.Hkv, "head_size": prob.hd, "block_size": prob.bs,
+           "kv_cache_dtype": prob.cache_dtype, "num_splits": splits, "cache_replicas": R,
+           "parallelism": "single GPU"}
+    line = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg, "roofline": roofline,
+            "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
