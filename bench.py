@@ -49,10 +49,10 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def make(name, bs):
+def make(name, bs, over=None):
     import workloads
     if name == "paged_decode":
-        return workloads.paged_decode()
+        return workloads.paged_decode(bs=bs or 16, **(over or {}))
     if name == "chunked_prefill":
         return workloads.chunked_prefill()
     if name == "long_decode":
@@ -92,12 +92,30 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="paged_decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--block-size", type=int, default=0, help="page size for fp8_decode (1, 8, 16, 64, 256)")
+    ap.add_argument("--block-size", type=int, default=0, help="page size for paged_decode / fp8_decode")
+    ap.add_argument("--batch", type=int, default=0, help="paged_decode: requests (default 64)")
+    ap.add_argument("--heads", type=int, default=0, help="paged_decode: query heads (default 32)")
+    ap.add_argument("--kv-heads", type=int, default=0, help="paged_decode: kv heads (default 8)")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--replicas", type=int, default=0, help="KV cache copies used in turn (0 = enough for 1.5 GB)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (default: the timed steps are one captured HIP graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}), flush=True)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the attention shards by request "
@@ -118,7 +136,8 @@ def main():
             return torch.from_numpy(a).to(dev).view(torch.float8_e4m3fn)
         return torch.from_numpy(a).to(dev)
     t0 = time.time()
-    prob = make(args.workload, args.block_size)
+    over = {k: v for k, v in (("B", args.batch), ("H", args.heads), ("Hkv", args.kv_heads)) if v}
+    prob = make(args.workload, args.block_size, over)
     log(f"[bench] workload {args.workload}: B={prob.B} T={prob.T} sumL={int(prob.seq_lens.sum())} "
         f"H={prob.H} Hkv={prob.Hkv} hd={prob.hd} bs={prob.bs} cache={prob.cache_dtype} "
         f"(generated in {time.time() - t0:.1f}s)")
@@ -177,6 +196,10 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    # Eager timed pass: the K steps launched one by one, with the library's
+    # HIP events around each attention kernel and each merge kernel (on the
+    # stream they are launched on). Kernel durations come from this pass.
     pkv.timing_enable(True)
     pkv.timing_collect()
     torch.cuda.synchronize()
@@ -184,12 +207,29 @@ def main():
     for i in range(args.steps):
         step(args.warmup + i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    ms_eager = (time.perf_counter() - t_start) * 1e3 / args.steps
     calls, main_ms, merge_ms = pkv.timing_collect()
     pkv.timing_enable(False)
-    ms_step = elapsed * 1e3 / args.steps
-    log(f"[bench] {args.steps} steps in {elapsed:.4f}s: {ms_step:.4f} ms/step; attention calls {calls}, "
-        f"main kernel {main_ms / max(calls, 1):.4f} ms avg, merge {merge_ms / max(calls, 1):.4f} ms avg")
+
+    use_graph = not args.eager and not cascade
+    if use_graph:
+        # The K timed steps captured into one HIP graph, as a serving engine
+        # captures its decode step: one untimed replay, then the timed replay.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(args.warmup + i)
+        graph.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    else:
+        ms_step = ms_eager
+    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step ({'graph' if use_graph else 'eager'}; eager "
+        f"{ms_eager:.4f}); attention calls {calls}, main kernel {main_ms / max(calls, 1):.4f} ms avg, "
+        f"merge {merge_ms / max(calls, 1):.4f} ms avg")
 
     decode_like = args.workload != "chunked_prefill"
     if decode_like:
@@ -264,9 +304,14 @@ def main():
                          f"{t_cpu:.1f}s"}
         log(f"[bench] oracle: {cpu}")
 
-    cfg = {"workload": WORKLOADS[args.workload], "global_batch": prob.B, "seq_len": prob.max_seqlen_k,
+    desc = WORKLOADS[args.workload]
+    if over or (args.block_size and args.workload == "paged_decode"):
+        desc = (f"paged decode, {prob.H}/{prob.Hkv} heads, head {prob.hd}, bf16, batch {prob.B}, "
+                f"ctx U[512,4096], page {prob.bs}")
+    cfg = {"workload": desc, "global_batch": prob.B, "seq_len": prob.max_seqlen_k,
            "num_heads": prob.H, "num_kv_heads": prob.Hkv, "head_size": prob.hd, "block_size": prob.bs,
            "kv_cache_dtype": prob.cache_dtype, "num_splits": splits, "cache_replicas": R,
+           "launch": "hip_graph" if use_graph else "eager", "ms_per_step_eager": round(ms_eager, 5),
            "parallelism": "single GPU"}
     line = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",

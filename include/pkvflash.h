@@ -153,13 +153,18 @@ size_t pkv_varlen_args_size(void);
 /* Validate `a` on the host only (no device access, no launch). */
 pkv_status pkv_varlen_check(const pkv_varlen_args* a);
 
-/* Number of KV splits pkv_varlen_fwd will use for `a` (1 when no split is
- * needed; 0 if the sizes in `a` are invalid), and the workspace bytes that
- * needs. Only the sizes, types and block_table/NULL choice of `a` are read:
- * the data pointers may be NULL here. The workspace
- * holds fp32 partial outputs [splits, num_tokens, num_heads, head_size] and
- * partial lse [splits, num_heads, num_tokens]; it is caller-owned and may be
- * reused between calls on one stream. */
+/* Number of KV partitions pkv_varlen_fwd will use for `a` (1 when the KV is
+ * not split; 0 if the sizes in `a` are invalid), and the workspace bytes that
+ * needs. Only the sizes, types and the block_table/NULL choice of `a` are
+ * read: the data pointers may be NULL here. The workspace is caller-owned,
+ * holds fp32 partial results and may be reused between calls on one stream.
+ * Decode batches (max_seqlen_q * num_heads / num_kv_heads <= 16, at most 1024
+ * requests) with num_splits == 0 use a balanced schedule: the 32-key KV tiles
+ * of all requests and kv heads are dealt out in equal shares to a fixed set
+ * of waves (the number returned), each writing a partial state per request
+ * segment it covers, which the merge kernel combines; without a large enough
+ * workspace such a batch runs unsplit. Other problems split each request's
+ * KV into equal key ranges. */
 int32_t pkv_varlen_num_splits(const pkv_varlen_args* a);
 size_t pkv_varlen_workspace_size(const pkv_varlen_args* a);
 

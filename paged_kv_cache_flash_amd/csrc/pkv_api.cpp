@@ -41,7 +41,7 @@ pkv_status hip_fail(hipError_t e, const char* what) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-enum class Kind { Decode, Prefill, Generic };
+enum class Kind { Decode, DecodeBalanced, Prefill, Generic };
 
 struct Plan {
     Kind kind;
@@ -112,6 +112,17 @@ Plan make_plan(const pkv_varlen_args* a) {
     const bool mfma = a->q_dtype == PKV_BF16 && mfma_head(a->head_size) && g <= kPrefillRows;
     int64_t items;
     int align;
+    if (mfma && (int64_t)a->max_seqlen_q * g <= kDecodeRows && a->num_splits == 0 &&
+        a->num_seqs <= kBalancedMaxSeqs) {
+        // balanced decode: kBalancedWaves waves share the KV tiles equally
+        pl.kind = Kind::DecodeBalanced;
+        pl.splits = kBalancedWaves;
+        pl.split_len = kDecodeTile;
+        const int64_t slots = kBalancedWaves + (int64_t)a->num_seqs * a->num_kv_heads;
+        pl.workspace = (size_t)slots * kDecodeRows * (a->head_size + 1) * sizeof(float) +
+                       (size_t)(a->num_seqs + 1) * sizeof(int32_t);
+        return pl;
+    }
     if (mfma && (int64_t)a->max_seqlen_q * g <= kDecodeRows) {
         pl.kind = Kind::Decode;
         items = (int64_t)a->num_seqs * a->num_kv_heads;
@@ -185,7 +196,15 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     pkv_status st = validate(a);
     if (st != PKV_OK || a->num_tokens == 0) return st;
     Plan pl = make_plan(a);
-    if (pl.splits > 1 && (a->workspace == nullptr || a->workspace_bytes < pl.workspace)) {
+    if (pl.kind == Kind::DecodeBalanced && (a->workspace == nullptr || a->workspace_bytes < pl.workspace)) {
+        // no room for the balanced schedule's partials: unsplit decode
+        pl.kind = Kind::Decode;
+        pl.splits = 1;
+        pl.split_len = (int32_t)std::max<int64_t>(a->block_table ? a->max_seqlen_k : a->max_seqlen_q, 1);
+        pl.workspace = 0;
+    }
+    if (pl.kind != Kind::DecodeBalanced && pl.splits > 1 &&
+        (a->workspace == nullptr || a->workspace_bytes < pl.workspace)) {
         if (a->num_splits > 1)
             return fail(PKV_ERR_WORKSPACE, "num_splits=%d needs %zu workspace bytes, got %zu", pl.splits, pl.workspace,
                         a->workspace ? a->workspace_bytes : (size_t)0);
@@ -219,7 +238,13 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     p.n_qtiles = pl.n_qtiles;
     p.causal = a->causal ? 1 : 0;
     p.scale_log2 = a->softmax_scale * 1.4426950408889634f;  // log2(e): kernels use exp2
-    if (pl.splits > 1) {
+    if (pl.kind == Kind::DecodeBalanced) {
+        const int64_t slots = kBalancedWaves + (int64_t)a->num_seqs * a->num_kv_heads;
+        p.sk_waves = kBalancedWaves;
+        p.part_o = (float*)a->workspace;
+        p.part_lse = p.part_o + (size_t)slots * kDecodeRows * a->head_size;
+        p.sk_prefix = (int32_t*)(p.part_lse + (size_t)slots * kDecodeRows);
+    } else if (pl.splits > 1) {
         p.part_o = (float*)a->workspace;
         p.part_lse = p.part_o + (size_t)pl.splits * a->num_tokens * a->num_heads * a->head_size;
     }
@@ -233,6 +258,7 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     }
     hipError_t e;
     switch (pl.kind) {
+        case Kind::DecodeBalanced: e = launch_decode_balanced(p, kv, s); break;
         case Kind::Decode: e = launch_decode(p, kv, s); break;
         case Kind::Prefill: e = launch_prefill(p, kv, s); break;
         default: e = launch_generic(p, kv, a->q_dtype == PKV_F32, s); break;
@@ -242,14 +268,15 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
         e = hipEventRecord(ev[1], s);
         if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
-    if (pl.splits > 1) {
+    const bool merge = pl.kind == Kind::DecodeBalanced || pl.splits > 1;
+    if (merge) {
         if (timed) (void)hipEventRecord(ev[2], s);
-        e = launch_combine(p, a->q_dtype == PKV_F32, s);
+        e = pl.kind == Kind::DecodeBalanced ? launch_combine_balanced(p, s) : launch_combine(p, a->q_dtype == PKV_F32, s);
         if (e != hipSuccess) return hip_fail(e, "split merge kernel launch");
         if (timed) (void)hipEventRecord(ev[3], s);
     }
     if (timed) {
-        g_tim.has_merge[g_tim.calls] = pl.splits > 1;
+        g_tim.has_merge[g_tim.calls] = merge;
         ++g_tim.calls;
     }
     return ok();

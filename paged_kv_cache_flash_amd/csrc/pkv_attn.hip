@@ -29,6 +29,8 @@
 //                  instantiation.
 //  combine_kernel  log-sum-exp merge of the split partials.
 //  merge_kernel    merge of two attention states (cascade prefix / suffix).
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_kernels.h"
 
@@ -61,45 +63,60 @@ __device__ __forceinline__ void store_f32(float* dst, const float* v) {
     for (int i = 0; i < N; i += 4) *(f32x4*)(dst + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
 }
 
-// 16 bytes of K or V for one row: 8 bf16 values (fp8 caches are widened; exact).
+// 8 elements of K or V as stored: 16 bytes of bf16 or 8 bytes of fp8.
+template <bool FP8>
+using raw8_t = typename std::conditional<FP8, u32x2, u32x4>::type;
+
+template <bool FP8>
+__device__ __forceinline__ raw8_t<FP8> load_raw8(const void* base, int64_t elem) {
+    if constexpr (FP8) return *(const u32x2*)((const uint8_t*)base + elem);
+    else return *(const u32x4*)((const uint16_t*)base + elem);
+}
+
+// Widen stored elements to 8 bf16 (exact for e4m3fn).
+template <bool FP8>
+__device__ __forceinline__ u32x4 to_bf16x8(raw8_t<FP8> r) {
+    if constexpr (FP8) return fp8x8_to_bf16x8(r);
+    else return r;
+}
+
 template <bool FP8>
 __device__ __forceinline__ u32x4 load_kv8(const void* base, int64_t elem) {
-    if constexpr (FP8) {
-        return fp8x8_to_bf16x8(*(const u32x2*)((const uint8_t*)base + elem));
-    } else {
-        return *(const u32x4*)((const uint16_t*)base + elem);
+    return to_bf16x8<FP8>(load_raw8<FP8>(base, elem));
+}
+
+// Request owning packed token `tok` (binary search over query_start_loc).
+__device__ __forceinline__ int request_of(const int32_t* qsl, int B, int64_t tok) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (qsl[mid] <= tok) lo = mid; else hi = mid - 1;
     }
+    return lo;
 }
 
 // ----------------------------------------------------------------- decode
 
-template <int HD, bool FP8>
-__global__ __launch_bounds__(256) void decode_kernel(FwdParams p) {
+// One wave's share of a decode work item: keys [k_first, k_end) of request r,
+// kv head kh, taken in 32-key tiles k_first, k_first + step, ... (step is a
+// multiple of 32). The item's query rows (q_len tokens x g heads of the group,
+// at most 16) are the columns of 16x16x32 MFMAs: S^T = K Q^T, O^T += V^T P^T.
+// Returns the wave's online-softmax state: m (log2 domain, row-uniform),
+// l (per lane: the sum over this lane's keys), and O^T (lane holds rows
+// l%16, head-dim elements 16*mb + 4*(l/16) + i).
+template <int HD, bool FP8, bool PAGED>
+__device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* vl, int lane, int r, int kh, int q0,
+                                             int q_len, int L, int k_first, int step, int k_end, float& m_run,
+                                             float& l_run, f32x4 (&oacc)[HD / 16]) {
     constexpr int TILE = kDecodeTile;
-    constexpr int NW = kDecodeWaves;
     constexpr int KS = HD / 32;             // k-steps of S^T = K Q^T
     constexpr int MB = HD / 16;             // 16-row blocks of O^T
     constexpr int VP = HD + 16;             // LDS pitch of a V row (bf16 elements)
     constexpr int CPR = HD / 8;             // 16-byte chunks per row
     constexpr int VLOADS = TILE * CPR / 64; // V chunks per lane per tile
     static_assert(HD % 32 == 0 && VLOADS >= 1, "");
-    constexpr int VSM = NW * TILE * VP;     // bf16 elements of V staging
-    constexpr int OSM = NW * 16 * HD * 2;   // the same bytes reused as fp32 partial outputs
-    __shared__ __attribute__((aligned(16))) uint16_t smem[VSM > OSM ? VSM : OSM];
-    __shared__ float sm_m[NW][16], sm_l[NW][16];
 
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
-    const int q0 = p.qsl[r];
-    const int q_len = p.qsl[r + 1] - q0;
-    if (q_len <= 0) return;
-    const int L = p.seq_lens ? p.seq_lens[r] : q_len;
     const int ctx = L - q_len;
-    const int k_begin = p.num_splits > 1 ? s * p.split_len : 0;
-    const int k_end = p.num_splits > 1 ? min(L, k_begin + p.split_len) : L;
-    if (k_begin >= k_end) return;  // no row of this item sees a key here; the merge never reads it
-
     const int g = p.g;
     const int row = lane & 15;
     const int G = lane >> 4;
@@ -116,47 +133,74 @@ __global__ __launch_bounds__(256) void decode_kernel(FwdParams p) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
     }
-    float sl2 = p.scale_log2, vsc = 1.f;
-    if constexpr (FP8) {
-        sl2 *= *p.k_scale;
-        vsc = *p.v_scale;
-    }
-    const int32_t* bt_row = p.bt ? p.bt + (int64_t)r * p.bt_stride : nullptr;
+    float sl2 = p.scale_log2;
+    if constexpr (FP8) sl2 *= *p.k_scale;
+    const int32_t* bt_row = PAGED ? p.bt + (int64_t)r * p.bt_stride : nullptr;
     const int64_t rstride = (int64_t)p.Hkv * HD;
     const int64_t hoff = (int64_t)kh * HD;
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 oacc[MB];
+    m_run = -INFINITY;
+    l_run = 0.f;
 #pragma unroll
     for (int i = 0; i < MB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint16_t* vl = smem + w * TILE * VP;
 
-    for (int t0 = k_begin + w * TILE; t0 < k_end; t0 += NW * TILE) {
-        // Each lane translates one key of the tile (lanes 32..63 repeat 0..31);
-        // the row indices are then shared with the lanes that load that key.
-        const int my_row = kv_row(bt_row, min(t0 + (lane & 31), L - 1), p.bs, q0);
-        u32x4 kf[2][KS];
+    // Address translation is split in two so that the block-table load of a
+    // tile can be issued a full tile ahead of its use: page_for issues the
+    // load of the block-table entry for the key this lane translates in tile t
+    // (lanes 32..63 repeat 0..31), row_from turns it into a cache row when the
+    // tile's loads are issued. (Using the entry right after loading it would
+    // make the wave wait for every load in flight, since loads retire in
+    // order.) Keys at or past the end of the range are clamped to its last
+    // key, so a prefetch past the end re-reads one cached row and every
+    // address stays inside the request's pages.
+    auto page_for = [&](int t) {
+        const int pos = min(t + (lane & 31), k_end - 1);
+        if constexpr (PAGED) return bt_row[pos / p.bs];
+        else return q0 + pos;
+    };
+    auto row_from = [&](int t, int page) {
+        const int pos = min(t + (lane & 31), k_end - 1);
+        if constexpr (PAGED) return page * p.bs + pos % p.bs;
+        else return page;
+    };
+    using raw_t = raw8_t<FP8>;
+    // K straight into MFMA A-operand registers, V as row-major 16-byte chunks
+    // for the LDS transpose.
+    auto load_tile = [&](int my_row, raw_t (&kf)[2][KS], raw_t (&vv)[VLOADS]) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int rb = __shfl(my_row, b * 16 + row);
             const int64_t e0 = (int64_t)rb * rstride + hoff + G * 8;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kf[b][ks] = load_kv8<FP8>(p.k_cache, e0 + ks * 32);
+            for (int ks = 0; ks < KS; ++ks) kf[b][ks] = load_raw8<FP8>(p.k_cache, e0 + ks * 32);
         }
-        u32x4 vv[VLOADS];
 #pragma unroll
         for (int i = 0; i < VLOADS; ++i) {
             const int c = lane + 64 * i;
             const int rv = __shfl(my_row, c / CPR);
-            vv[i] = load_kv8<FP8>(p.v_cache, (int64_t)rv * rstride + hoff + (c % CPR) * 8);
+            vv[i] = load_raw8<FP8>(p.v_cache, (int64_t)rv * rstride + hoff + (c % CPR) * 8);
         }
+    };
+    // V of a tile: registers -> LDS, row-major (read back transposed)
+    auto store_v = [&](const raw_t (&vv)[VLOADS]) {
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < VLOADS; ++i) {
+            const int c = lane + 64 * i;
+            *(u32x4*)(vl + (c / CPR) * VP + (c % CPR) * 8) = to_bf16x8<FP8>(vv[i]);
+        }
+        wave_lds_sync();
+    };
+    // One tile: S^T from K in registers, online softmax, O^T += V^T P^T with
+    // V^T read transposed from LDS.
+    auto compute_tile = [&](int t0, const raw_t (&kf)[2][KS]) {
         // S^T[key][row] for two 16-key blocks
         f32x4 sacc[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             sacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sacc[b] = mfma16x16x32(kf[b][ks], qf[ks], sacc[b]);
+            for (int ks = 0; ks < KS; ++ks) sacc[b] = mfma16x16x32(to_bf16x8<FP8>(kf[b][ks]), qf[ks], sacc[b]);
         }
         float sv[8];
         float mx = -INFINITY;
@@ -187,14 +231,6 @@ __global__ __launch_bounds__(256) void decode_kernel(FwdParams p) {
         // P^T as the B operand: k-slot 8*G + j holds key 16*(j/4) + 4*G + j%4
         const u32x4 pf = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]), pack_bf16x2(sv[4], sv[5]),
                           pack_bf16x2(sv[6], sv[7])};
-        // V tile -> LDS (row-major), then V^T fragments by transposed reads
-        wave_lds_sync();
-#pragma unroll
-        for (int i = 0; i < VLOADS; ++i) {
-            const int c = lane + 64 * i;
-            *(u32x4*)(vl + (c / CPR) * VP + (c % CPR) * 8) = vv[i];
-        }
-        wave_lds_sync();
         const uint16_t* vt = vl + (G * 4 + ((lane & 15) >> 2)) * VP + (lane & 3) * 4;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -202,9 +238,82 @@ __global__ __launch_bounds__(256) void decode_kernel(FwdParams p) {
             const u32x2 hi = lds_read_tr16(vt + 16 * VP + mb * 16);
             oacc[mb] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, oacc[mb]);
         }
+    };
+
+    // Software pipeline over the wave's tiles. Iteration i: request the
+    // block-table entry of tile i+2, issue the K/V loads of tile i+1
+    // (unconditionally: past the end they re-read a cached row), compute tile
+    // i (K in registers, V already in LDS), turn the block-table entry into a
+    // row index, and move tile i+1's V into LDS. K is double-buffered in
+    // registers, V single-buffered (it leaves the registers each iteration).
+    // Every load result is consumed in the iteration that issued it, so the
+    // wait before a compute covers the current tile only.
+    int t_cur = k_first;
+    if (t_cur < k_end) {
+        raw_t ka[2][KS], kb[2][KS], vv[VLOADS];
+        const int row0 = row_from(t_cur, page_for(t_cur));
+        const int pg1 = page_for(t_cur + step);
+        load_tile(row0, ka, vv);
+        int row1 = row_from(t_cur + step, pg1);
+        store_v(vv);
+        while (true) {
+            int pg2 = page_for(t_cur + 2 * step);
+            load_tile(row1, kb, vv);
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
+            compute_tile(t_cur, ka);
+            row1 = row_from(t_cur + 2 * step, pg2);
+            store_v(vv);
+            __builtin_amdgcn_sched_barrier(0);
+            t_cur += step;
+            if (t_cur >= k_end) break;
+            pg2 = page_for(t_cur + 2 * step);
+            load_tile(row1, ka, vv);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_tile(t_cur, kb);
+            row1 = row_from(t_cur + 2 * step, pg2);
+            store_v(vv);
+            __builtin_amdgcn_sched_barrier(0);
+            t_cur += step;
+            if (t_cur >= k_end) break;
+        }
     }
+    // per-row sum over the four lane groups
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
+}
+
+// Split-KV decode: one workgroup per (KV split, kv head, request); its four
+// waves take interleaved tiles of the split and merge their states in LDS.
+template <int HD, bool FP8, bool PAGED>
+__global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParams p) {
+    constexpr int TILE = kDecodeTile;
+    constexpr int NW = kDecodeWaves;
+    constexpr int MB = HD / 16;
+    constexpr int VP = HD + 16;
+    constexpr int VSM = NW * TILE * VP;     // bf16 elements of V staging
+    constexpr int OSM = NW * 16 * HD * 2;   // the same bytes reused as fp32 partial outputs
+    __shared__ __attribute__((aligned(16))) uint16_t smem[VSM > OSM ? VSM : OSM];
+    __shared__ float sm_m[NW][16], sm_l[NW][16];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
+    const int q0 = p.qsl[r];
+    const int q_len = p.qsl[r + 1] - q0;
+    if (q_len <= 0) return;
+    const int L = p.seq_lens ? p.seq_lens[r] : q_len;
+    const int k_begin = p.num_splits > 1 ? s * p.split_len : 0;
+    const int k_end = p.num_splits > 1 ? min(L, k_begin + p.split_len) : L;
+    if (k_begin >= k_end) return;  // no row of this item sees a key here; the merge never reads it
+
+    float m_run, l_run;
+    f32x4 oacc[MB];
+    decode_range<HD, FP8, PAGED>(p, smem + w * TILE * VP, lane, r, kh, q0, q_len, L, k_begin + w * TILE, NW * TILE,
+                                 k_end, m_run, l_run, oacc);
+    const int row = lane & 15;
+    const int G = lane >> 4;
+    const int g = p.g;
+    const int rows_total = q_len * g;
 
     // merge the four waves' states
     __syncthreads();
@@ -221,6 +330,7 @@ __global__ __launch_bounds__(256) void decode_kernel(FwdParams p) {
     const int frow = threadIdx.x >> 4;
     const int fc = (threadIdx.x & 15) * PER;
     if (frow >= rows_total) return;
+    const float vsc = FP8 ? *p.v_scale : 1.f;
     float M = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i][frow]);
@@ -249,6 +359,132 @@ __global__ __launch_bounds__(256) void decode_kernel(FwdParams p) {
     } else {
         store_f32<PER>(p.part_o + (((int64_t)s * p.T + tok) * p.H + head) * HD + fc, o);
         if ((threadIdx.x & 15) == 0) p.part_lse[((int64_t)s * p.H + head) * p.T + tok] = lse;
+    }
+}
+
+// ------------------------------------------------- decode, balanced schedule
+//
+// Every (request, kv head) item of decode is a row of 32-key tiles; the items
+// are laid end to end (request-major, then kv head) into one list of N tiles
+// and wave w of the grid takes tiles [w N / W, (w+1) N / W), whatever items
+// they belong to. Each wave therefore streams the same number of bytes, and
+// the grid is sized to be resident at once. A wave writes one partial state
+// per item segment it covers, into slot (w + item); when it covers a whole
+// item it writes the final output instead. The merge kernel then combines,
+// for each row, the partials of the waves wave_of(first tile of its item) ..
+// wave_of(last tile), which are exactly the waves that wrote them.
+
+__device__ __forceinline__ int decode_tiles_of(const FwdParams& p, int r) {
+    const int ql = p.qsl[r + 1] - p.qsl[r];
+    if (ql <= 0) return 0;
+    const int L = p.seq_lens ? p.seq_lens[r] : ql;
+    return (L + kDecodeTile - 1) / kDecodeTile;
+}
+
+// Wave index whose tile range holds global tile t (ranges [w N / W, (w+1) N / W)).
+__device__ __forceinline__ int64_t wave_of_tile(int64_t t, int64_t N, int64_t W) { return ((t + 1) * W - 1) / N; }
+
+template <int HD, bool FP8, bool PAGED>
+__global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel(FwdParams p) {
+    constexpr int TILE = kDecodeTile;
+    constexpr int MB = HD / 16;
+    constexpr int VP = HD + 16;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE * VP];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + w;
+    const int64_t W = (int64_t)gridDim.x * 4;
+
+    // total tiles, then the request holding this wave's first tile; wave 0
+    // also publishes the per-request tile prefix for the merge kernel
+    int total = 0;
+    for (int base = 0; base < p.B; base += 64) {
+        int n = base + lane < p.B ? decode_tiles_of(p, base + lane) : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+        total += n;
+    }
+    const int64_t N = (int64_t)p.Hkv * total;
+    const int64_t T0 = gw * N / W, T1 = (gw + 1) * N / W;
+    int r = -1, pr = 0, carry = 0;
+    for (int base = 0; base < p.B; base += 64) {
+        const int rr = base + lane;
+        const int n = rr < p.B ? decode_tiles_of(p, rr) : 0;
+        int incl = n;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const int excl = carry + incl - n;
+        if (gw == 0 && rr < p.B) p.sk_prefix[rr] = excl;
+        const bool here = n > 0 && (int64_t)p.Hkv * excl <= T0 && T0 < (int64_t)p.Hkv * (excl + n);
+        const uint64_t bal = __ballot(here);
+        if (bal != 0 && r < 0) {
+            const int src = __ffsll((unsigned long long)bal) - 1;
+            r = base + src;
+            pr = __shfl(excl, src);
+        }
+        carry += __shfl(incl, 63);
+    }
+    if (gw == 0 && lane == 0) p.sk_prefix[p.B] = carry;
+    if (T0 >= T1 || r < 0) return;
+
+    int n_r = decode_tiles_of(p, r);
+    const int64_t off = T0 - (int64_t)p.Hkv * pr;
+    int kh = (int)(off / n_r);
+    int t = (int)(off % n_r);
+    int64_t T = T0;
+    uint16_t* vl = smem + w * TILE * VP;
+    const int row = lane & 15;
+    const int G = lane >> 4;
+    const float vsc = FP8 ? *p.v_scale : 1.f;
+    while (true) {
+        const int cnt = (int)min((int64_t)(n_r - t), T1 - T);
+        const int q0 = p.qsl[r];
+        const int q_len = p.qsl[r + 1] - q0;
+        const int L = p.seq_lens ? p.seq_lens[r] : q_len;
+        const int k_end = min(L, (t + cnt) * TILE);
+        float m_run, l_run;
+        f32x4 oacc[MB];
+        decode_range<HD, FP8, PAGED>(p, vl, lane, r, kh, q0, q_len, L, t * TILE, TILE, k_end, m_run, l_run, oacc);
+        const int rows_total = q_len * p.g;
+        if (row < rows_total) {
+            const float inv = l_run > 0.f ? vsc / l_run : 0.f;
+            const float mu = m_run == -INFINITY ? 0.f : m_run;
+            const float lse = l_run > 0.f ? (mu + fast_log2(l_run)) * kLn2 : -INFINITY;
+            if (t == 0 && cnt == n_r) {  // the whole item: final output
+                const int64_t tok = q0 + row / p.g;
+                const int head = kh * p.g + row % p.g;
+                uint16_t* op = (uint16_t*)p.out + (tok * p.H + head) * HD + G * 4;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    float v4[4] = {oacc[mb][0] * inv, oacc[mb][1] * inv, oacc[mb][2] * inv, oacc[mb][3] * inv};
+                    store_bf16<4>(op + mb * 16, v4);
+                }
+                if (p.lse && G == 0) p.lse[(int64_t)head * p.T + tok] = lse;
+            } else {  // a segment: partial state into slot (wave + item)
+                const int64_t slot = gw + (int64_t)r * p.Hkv + kh;
+                float* op = p.part_o + (slot * 16 + row) * HD + G * 4;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) *(f32x4*)(op + mb * 16) = oacc[mb] * inv;
+                if (G == 0) p.part_lse[slot * 16 + row] = lse;
+            }
+        }
+        T += cnt;
+        if (T >= T1) break;
+        t += cnt;
+        if (t == n_r) {
+            t = 0;
+            if (++kh == p.Hkv) {
+                kh = 0;
+                do {
+                    ++r;
+                    n_r = r < p.B ? decode_tiles_of(p, r) : 1;
+                } while (n_r == 0);
+                if (r >= p.B) break;  // only on metadata that contradicts itself
+            }
+        }
     }
 }
 
@@ -437,15 +673,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(FwdParams p) {
 
 // ----------------------------------------------------------------- generic
 
-__device__ __forceinline__ int request_of(const int32_t* qsl, int B, int64_t tok) {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (qsl[mid] <= tok) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
 template <KvType KV>
 __device__ __forceinline__ float load_kv1(const void* base, int64_t e) {
     if constexpr (KV == KvType::F32) return ((const float*)base)[e];
@@ -535,17 +762,19 @@ __global__ __launch_bounds__(64) void generic_kernel(FwdParams p) {
 
 // ----------------------------------------------------------------- combine
 
-// One thread per 4 output elements. Split s of a row holds keys
-// [s * split_len, (s+1) * split_len); only splits below ceil(n_vis / split_len)
-// were written, and only those are read.
+// Merge of the split partials. Split s of a row holds keys
+// [s * split_len, (s+1) * split_len); only splits below
+// ceil(n_vis / split_len) were written, and only those are read.
+// One half-wave (32 lanes) per (token, head) row: lane j first holds the lse
+// of splits j, j+32, ... and their weights, then the lanes accumulate
+// 4-element chunks of the row over all splits, with independent loads.
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int cpr = p.hd / 4;
-    const int64_t nrow = p.T * p.H;
-    if (idx >= nrow * cpr) return;
-    const int64_t rowi = idx / cpr;
-    const int c = (int)(idx % cpr);
+    constexpr int MAXC = 8;  // up to 256 splits, 32 per lane-chunk
+    const int lane = threadIdx.x & 63;
+    const int hl = lane & 31;
+    const int64_t rowi = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;
+    if (rowi >= p.T * p.H) return;  // whole half-waves leave together
     const int64_t tok = rowi / p.H;
     const int h = (int)(rowi % p.H);
     const int r = request_of(p.qsl, p.B, tok);
@@ -555,29 +784,141 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
     const int t = (int)(tok - q0);
     const int n_vis = p.causal ? max(0, min(L, L - q_len + t + 1)) : L;
     const int n_valid = min(p.num_splits, (n_vis + p.split_len - 1) / p.split_len);
+    const int nc = (n_valid + 31) >> 5;
+    float ls[MAXC];
     float M = -INFINITY;
-    for (int s = 0; s < n_valid; ++s) M = fmaxf(M, p.part_lse[((int64_t)s * p.H + h) * p.T + tok]);
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    float lse = -INFINITY;
-    if (M != -INFINITY) {
-        float sum = 0.f;
-        for (int s = 0; s < n_valid; ++s) {
-            const float ls = p.part_lse[((int64_t)s * p.H + h) * p.T + tok];
-            const float wgt = fast_exp2((ls - M) * kLog2e);
-            sum += wgt;
-            const f32x4 v = *(const f32x4*)(p.part_o + (((int64_t)s * p.T + tok) * p.H + h) * p.hd + 4 * c);
-            o += wgt * v;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int sp = c * 32 + hl;
+        ls[c] = (c < nc && sp < n_valid) ? p.part_lse[((int64_t)sp * p.H + h) * p.T + tok] : -INFINITY;
+        M = fmaxf(M, ls[c]);
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float wsum = 0.f;
+    const float Mu = M == -INFINITY ? 0.f : M;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        ls[c] = fast_exp2((ls[c] - Mu) * kLog2e);  // weight of split c*32 + hl (0 if absent)
+        wsum += ls[c];
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const float lse = wsum > 0.f ? M + fast_log2(wsum) * kLn2 : -INFINITY;
+    const int nch = p.hd / 4;  // 4-element chunks per row (<= 64)
+    const int base_lane = lane & 32;
+    for (int cc = hl; cc < ((nch + 31) & ~31); cc += 32) {
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < nc; ++c) {
+            const int cnt = min(32, n_valid - c * 32);
+            for (int j = 0; j < cnt; ++j) {
+                const float wgt = __shfl(ls[c], base_lane + j);
+                const int sp = c * 32 + j;
+                if (cc < nch) o += wgt * *(const f32x4*)(p.part_o + (((int64_t)sp * p.T + tok) * p.H + h) * p.hd + 4 * cc);
+            }
         }
-        o *= 1.f / sum;
-        lse = M + fast_log2(sum) * kLn2;
+        if (cc < nch) {
+            o *= inv;
+            const int64_t e = (tok * p.H + h) * p.hd + 4 * cc;
+            if (OUT_F32) *(f32x4*)((float*)p.out + e) = o;
+            else *(u32x2*)((uint16_t*)p.out + e) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        }
     }
-    const int64_t e = (tok * p.H + h) * p.hd + 4 * c;
-    if (OUT_F32) {
-        *(f32x4*)((float*)p.out + e) = o;
-    } else {
-        *(u32x2*)((uint16_t*)p.out + e) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    if (p.lse && hl == 0) p.lse[(int64_t)h * p.T + tok] = lse;
+}
+
+// Merge for the balanced decode schedule: one half-wave per row of a
+// (request, kv head) item, two workgroups of eight half-waves per item (up to
+// 16 rows). The item was covered by waves wave_of(first tile) ..
+// wave_of(last tile) (those that own at least one tile); with one wave the
+// output is already final. The item comes from the block index, so the
+// metadata loads are independent of each other.
+__global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
+    const int lane = threadIdx.x & 63;
+    const int hl = lane & 31;
+    const int base_lane = lane & 32;
+    const int64_t item = blockIdx.x >> 1;
+    const int r = (int)(item / p.Hkv);
+    const int kh = (int)(item % p.Hkv);
+    const int row16 = (int)((blockIdx.x & 1) * 8 + (threadIdx.x >> 5));
+    const int q0 = p.qsl[r];
+    const int q_len = p.qsl[r + 1] - q0;
+    if (row16 >= q_len * p.g) return;  // whole half-waves leave together
+    const int L = p.seq_lens ? p.seq_lens[r] : q_len;
+    const int64_t N = (int64_t)p.Hkv * p.sk_prefix[p.B];
+    const int64_t first = (int64_t)p.Hkv * p.sk_prefix[r];
+    const int n_r = (L + kDecodeTile - 1) / kDecodeTile;
+    const int64_t W = p.sk_waves;
+    const int64_t g0 = first + (int64_t)kh * n_r;
+    const int64_t wf = wave_of_tile(g0, N, W), wl = wave_of_tile(g0 + n_r - 1, N, W);
+    if (wf == wl) return;
+    const int64_t tok = q0 + row16 / p.g;
+    const int h = kh * p.g + row16 % p.g;
+    const int64_t slot0 = wf + item;
+    const int np = (int)(wl - wf + 1);
+    // with more waves than tiles some waves own no tile and wrote nothing
+    auto owns_tiles = [&](int64_t w) { return (w + 1) * N / W > w * N / W; };
+    float lsv[2];
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int j = hl + 32 * c;
+        lsv[c] = (j < np && owns_tiles(wf + j)) ? p.part_lse[(slot0 + j) * 16 + row16] : -INFINITY;
+        M = fmaxf(M, lsv[c]);
     }
-    if (p.lse && c == 0) p.lse[(int64_t)h * p.T + tok] = lse;
+    for (int j = hl + 64; j < np; j += 32)
+        if (owns_tiles(wf + j)) M = fmaxf(M, p.part_lse[(slot0 + j) * 16 + row16]);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const int nch = p.hd / 4;
+    const bool c0 = hl < nch, c1 = hl + 32 < nch;
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    for (int j0 = 0; j0 < np; j0 += 32) {
+        const int j = j0 + hl;
+        float ls;
+        if (j0 < 64) ls = lsv[j0 >> 5];
+        else ls = (j < np && owns_tiles(wf + j)) ? p.part_lse[(slot0 + j) * 16 + row16] : -INFINITY;
+        const float wj = fast_exp2((ls - Mu) * kLog2e);  // 0 for absent partials
+        wsum += wj;
+        const int cnt = min(32, np - j0);
+        // four partials per step, their loads issued together
+        for (int k = 0; k < cnt; k += 4) {
+            f32x4 v0[4], v1[4];
+            float wk[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                wk[u] = __shfl(wj, base_lane + min(k + u, cnt - 1));
+                if (k + u >= cnt) wk[u] = 0.f;
+                const float* src = p.part_o + ((slot0 + j0 + min(k + u, cnt - 1)) * 16 + row16) * p.hd;
+                v0[u] = c0 ? *(const f32x4*)(src + 4 * hl) : f32x4{0.f, 0.f, 0.f, 0.f};
+                v1[u] = c1 ? *(const f32x4*)(src + 4 * (hl + 32)) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                // an absent partial's slot holds stale bytes: select, never multiply by 0
+                if (wk[u] != 0.f) {
+                    o0 += wk[u] * v0[u];
+                    o1 += wk[u] * v1[u];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    uint16_t* dst = (uint16_t*)p.out + (tok * p.H + h) * p.hd;
+    if (c0) {
+        o0 *= inv;
+        *(u32x2*)(dst + 4 * hl) = u32x2{pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3])};
+    }
+    if (c1) {
+        o1 *= inv;
+        *(u32x2*)(dst + 4 * (hl + 32)) = u32x2{pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
+    }
+    if (p.lse && hl == 0) p.lse[(int64_t)h * p.T + tok] = wsum > 0.f ? M + fast_log2(wsum) * kLn2 : -INFINITY;
 }
 
 template <bool F32>
@@ -624,8 +965,43 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, float* out_lse, c
 template <int HD>
 static hipError_t decode_hd(const FwdParams& p, KvType kv, hipStream_t s) {
     dim3 grid(p.num_splits, p.Hkv, p.B);
-    if (kv == KvType::FP8) hipLaunchKernelGGL((decode_kernel<HD, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<HD, false>), grid, dim3(256), 0, s, p);
+    const bool paged = p.bt != nullptr;
+    if (kv == KvType::FP8) {
+        if (paged) hipLaunchKernelGGL((decode_kernel<HD, true, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((decode_kernel<HD, true, false>), grid, dim3(256), 0, s, p);
+    } else {
+        if (paged) hipLaunchKernelGGL((decode_kernel<HD, false, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((decode_kernel<HD, false, false>), grid, dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t decode_balanced_hd(const FwdParams& p, KvType kv, hipStream_t s) {
+    dim3 grid(p.sk_waves / 4);
+    const bool paged = p.bt != nullptr;
+    if (kv == KvType::FP8) {
+        if (paged) hipLaunchKernelGGL((decode_balanced_kernel<HD, true, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((decode_balanced_kernel<HD, true, false>), grid, dim3(256), 0, s, p);
+    } else {
+        if (paged) hipLaunchKernelGGL((decode_balanced_kernel<HD, false, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((decode_balanced_kernel<HD, false, false>), grid, dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_balanced(const FwdParams& p, KvType kv, hipStream_t s) {
+    switch (p.hd) {
+        case 64: return decode_balanced_hd<64>(p, kv, s);
+        case 128: return decode_balanced_hd<128>(p, kv, s);
+        case 256: return decode_balanced_hd<256>(p, kv, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_combine_balanced(const FwdParams& p, hipStream_t s) {
+    const int64_t items = (int64_t)p.B * p.Hkv;  // two workgroups (16 row slots) per item
+    hipLaunchKernelGGL(combine_balanced_kernel, dim3((unsigned)(2 * items)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -664,7 +1040,7 @@ hipError_t launch_generic(const FwdParams& p, KvType kv, bool q_f32, hipStream_t
 }
 
 hipError_t launch_combine(const FwdParams& p, bool out_f32, hipStream_t s) {
-    const int64_t n = p.T * p.H * (p.hd / 4);
+    const int64_t n = p.T * p.H * 32;  // a half-wave per (token, head) row
     dim3 grid((unsigned)((n + 255) / 256));
     if (out_f32) hipLaunchKernelGGL((combine_kernel<true>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, s, p);

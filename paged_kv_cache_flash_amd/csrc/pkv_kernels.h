@@ -27,12 +27,17 @@ struct FwdParams {
     int32_t n_qtiles;         // prefill: query tiles per (request, kv head)
     int32_t causal;
     float scale_log2;         // softmax_scale * log2(e)
+    // balanced decode schedule
+    int32_t sk_waves;         // waves sharing the decode tiles (grid = sk_waves / 4 workgroups)
+    int32_t* sk_prefix;       // [B+1] per-request tile prefix and total, written by the attention kernel
 };
 
 enum class KvType { BF16, FP8, F32 };
 
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_decode(const FwdParams& p, KvType kv, hipStream_t s);
+hipError_t launch_decode_balanced(const FwdParams& p, KvType kv, hipStream_t s);
+hipError_t launch_combine_balanced(const FwdParams& p, hipStream_t s);
 hipError_t launch_prefill(const FwdParams& p, KvType kv, hipStream_t s);
 hipError_t launch_generic(const FwdParams& p, KvType kv, bool q_f32, hipStream_t s);
 hipError_t launch_combine(const FwdParams& p, bool out_f32, hipStream_t s);
@@ -47,6 +52,10 @@ hipError_t launch_cache_write(const void* key, const void* value, int src_f32, v
 constexpr int kDecodeRows = 16;
 constexpr int kDecodeTile = 32;
 constexpr int kDecodeWaves = 4;
+// Balanced decode: waves in the grid (256 CUs x 8 resident waves on MI355X)
+// and the largest batch whose schedule each wave derives by itself.
+constexpr int kBalancedWaves = 2048;
+constexpr int kBalancedMaxSeqs = 1024;
 // Prefill kernel geometry.
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillWaves = 4;

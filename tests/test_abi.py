@@ -101,18 +101,25 @@ def test_null_args_pointer():
 
 def test_split_plan_and_workspace():
     L = pkv.lib()
-    # long-context decode with few work items is split; the workspace holds
-    # fp32 partial outputs and lse per split
+    # decode with num_splits == 0 takes the balanced schedule: 2048 waves share
+    # the KV tiles; the workspace holds a 16-row fp32 partial (+ lse) per
+    # (wave + item) slot and the per-request tile prefix
     a = good_args(num_tokens=4, num_seqs=4, num_heads=64, num_kv_heads=8, max_seqlen_k=131072,
                   block_size=256, block_table_stride=512, num_blocks=4096)
-    s = L.pkv_varlen_num_splits(ctypes.byref(a))
-    assert 16 <= s <= 64
-    assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == s * 4 * 64 * (128 + 1) * 4
+    assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 2048
+    assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == (2048 + 4 * 8) * 16 * (128 + 1) * 4 + (4 + 1) * 4
     a.num_splits = 1
     assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 1
     assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == 0
     a.num_splits = 7
     assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 7
+    assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == 7 * 4 * 64 * (128 + 1) * 4
+    # a long prefill of one request with few query tiles is split by key range
+    b = good_args(num_tokens=256, num_seqs=1, num_heads=8, num_kv_heads=8, max_seqlen_q=256, max_seqlen_k=65536,
+                  block_size=16, block_table_stride=4096, num_blocks=5000)
+    s = L.pkv_varlen_num_splits(ctypes.byref(b))
+    assert 2 <= s <= 64
+    assert L.pkv_varlen_workspace_size(ctypes.byref(b)) == s * 256 * 8 * (128 + 1) * 4
 
 
 def test_forced_split_without_workspace_is_an_error():
