@@ -109,7 +109,7 @@ Plan make_plan(const pkv_varlen_args* a) {
     const int g = a->num_heads / a->num_kv_heads;
     const bool paged = a->block_table != nullptr;
     const int64_t max_k = paged ? a->max_seqlen_k : a->max_seqlen_q;
-    const bool mfma = a->q_dtype == PKV_BF16 && mfma_head(a->head_size) && g <= kPrefillRows;
+    const bool mfma = a->q_dtype == PKV_BF16 && mfma_head(a->head_size) && g <= kPrefillMaxGroup;
     int64_t items;
     int align;
     if (mfma && (int64_t)a->max_seqlen_q * g <= kDecodeRows && a->num_splits == 0 &&
@@ -129,10 +129,10 @@ Plan make_plan(const pkv_varlen_args* a) {
         align = kDecodeTile * kDecodeWaves;
     } else if (mfma) {
         pl.kind = Kind::Prefill;
-        const int tpw = kPrefillRows / g;
+        const int tpw = prefill_rows(a->head_size) / g;
         pl.n_qtiles = (int32_t)cdiv(a->max_seqlen_q, tpw);
         items = (int64_t)a->num_seqs * a->num_kv_heads * pl.n_qtiles;
-        align = kPrefillTile * 4;
+        align = prefill_tile(a->head_size) * 4;
     } else {
         pl.kind = Kind::Generic;
         items = a->num_tokens * a->num_heads;
@@ -142,10 +142,13 @@ Plan make_plan(const pkv_varlen_args* a) {
     if (a->num_splits > 1) {
         S = a->num_splits;
     } else if (a->num_splits == 0 && pl.kind != Kind::Generic) {
-        // Enough workgroups to fill 256 CUs several times over, but at least
-        // 512 keys of work per split.
+        // Split only when there are too few work items to occupy 256 CUs, and
+        // keep at least 512 keys of work per split. (Prefill partials are
+        // written for every query row, so splitting a prefill that already
+        // fills the chip costs far more traffic than it saves.)
         const int64_t by_len = cdiv(max_k, 512);
-        if (items < 2048) S = std::min<int64_t>(by_len, std::max<int64_t>(1, cdiv(4096, items)));
+        const int64_t enough = pl.kind == Kind::Prefill ? 256 : 2048;
+        if (items < enough) S = std::min<int64_t>(by_len, std::max<int64_t>(1, cdiv(2 * enough, items)));
         S = std::max<int64_t>(1, std::min<int64_t>(S, 64));
     }
     if (S > 1) {
@@ -233,6 +236,9 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     p.g = a->num_heads / a->num_kv_heads;
     p.hd = a->head_size;
     p.bs = a->block_table ? a->block_size : 1;
+    p.bs_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == p.bs) p.bs_shift = sh;
     p.num_splits = pl.splits;
     p.split_len = pl.split_len;
     p.n_qtiles = pl.n_qtiles;

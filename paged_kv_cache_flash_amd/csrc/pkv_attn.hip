@@ -21,9 +21,10 @@
 //                  transposed; the waves merge their states through LDS.
 //  prefill_kernel  one work item = (request, kv head, 128 query rows, KV split);
 //                  rows are (token, head-of-group) pairs, 32 per wave, on
-//                  32x32x16 bf16 MFMA; K/V tiles are staged in LDS for all
-//                  four waves; tiles entirely in a wave's future are skipped
-//                  and only tiles crossing the diagonal build a per-element mask.
+//                  32x32x16 bf16 MFMA; 64-key K/V tiles are copied from HBM
+//                  straight into padded chunk-major LDS (two slots each, one
+//                  tile ahead) and shared by the four waves; only tiles crossing the diagonal
+//                  build a per-element mask.
 //  generic_kernel  one wave per (token, head); plain fp32 arithmetic on the
 //                  vector ALUs for fp32 inputs and head sizes without an MFMA
 //                  instantiation.
@@ -155,12 +156,12 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* vl, i
     // address stays inside the request's pages.
     auto page_for = [&](int t) {
         const int pos = min(t + (lane & 31), k_end - 1);
-        if constexpr (PAGED) return bt_row[pos / p.bs];
+        if constexpr (PAGED) return bt_row[page_index(pos, p.bs, p.bs_shift)];
         else return q0 + pos;
     };
     auto row_from = [&](int t, int page) {
         const int pos = min(t + (lane & 31), k_end - 1);
-        if constexpr (PAGED) return page * p.bs + pos % p.bs;
+        if constexpr (PAGED) return page * p.bs + page_offset(pos, p.bs, p.bs_shift);
         else return page;
     };
     using raw_t = raw8_t<FP8>;
@@ -490,31 +491,71 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
 
 // ----------------------------------------------------------------- prefill
 
-template <int HD, bool FP8>
-__global__ __launch_bounds__(256) void prefill_kernel(FwdParams p) {
-    constexpr int TILE = kPrefillTile;
-    constexpr int KP = HD + 8;          // LDS pitch of K rows (bf16 elements)
-    constexpr int VP = HD + 16;         // LDS pitch of V rows
-    constexpr int CPR = HD / 8;
-    constexpr int LPT = TILE * CPR / 256;  // 16-byte chunks of K (and of V) per thread per tile
-    constexpr int KS = HD / 16;         // k-steps of S^T = K Q^T (32x32x16)
-    constexpr int MB = HD / 32;         // 32-row blocks of O^T
-    static_assert(HD % 32 == 0 && LPT >= 1, "");
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[TILE * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[TILE * VP];
+// Rescale of the running output is skipped until a row's running maximum
+// grows by more than this (log2 units): probabilities are then formed against
+// a stale maximum and stay below 2^8, and the final normalisation by the same
+// stale maximum keeps the result exact.
+constexpr float kLazyRescale = 8.f;
+
+// One 16-byte global -> LDS copy per lane, written by the load unit straight
+// into LDS at lds_base + 16 * lane (lds_base must be wave-uniform); `off` is
+// added to the global address.
+template <int OFF>
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, OFF, 0);
+}
+
+// K/V tiles of 64 keys live in LDS chunk-major: the 16-byte chunk c (8 bf16
+// elements) of tile row r is at c * kChunkPitch + 16 r, each chunk column
+// padded by 64 bytes. A 16-byte K fragment read (16 consecutive rows of one
+// chunk per 16 lanes) is then contiguous, and a transposed V read (4 rows x 4
+// chunks per 16 lanes) lands the four chunk columns 64 bytes apart, so
+// neither has bank conflicts. Lane l of a 64-lane copy moves tile row l.
+constexpr int kTileRows = 64;
+constexpr int kChunkPitch = kTileRows * 16 + 64;
+
+// POW2: the page size is a power of two (or the layout is flat), so a key's
+// page and offset come from a shift and a mask.
+template <int HD, bool FP8, bool POW2>
+__global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdParams p) {
+    constexpr int NW = kPrefillWaves;           // waves per workgroup
+    constexpr int ROWS = prefill_rows(HD);      // query rows per work item
+    constexpr int TILE = prefill_tile(HD);      // keys per tile
+    constexpr int CPR = HD / 8;                 // 16-byte chunks per row
+    constexpr int CPW = CPR / NW;               // chunk columns each wave copies per tile
+    constexpr int KS = HD / 16;                 // k-steps of S^T = K Q^T (32x32x16)
+    constexpr int MB = HD / 32;                 // 32-row blocks of O^T
+    constexpr int KB = TILE / 32;               // 32-key blocks per tile
+    constexpr int SLOT = CPR * kChunkPitch;     // bytes of one K or V tile
+    constexpr int ESZ = FP8 ? 1 : 2;            // bytes per cached element
+    static_assert(TILE == kTileRows && CPW >= 1 && CPR % NW == 0, "");
+    // K tile j in k_lds<j % 2>, V tile j in v_lds<j % 2>; four separate arrays
+    // so that the compiler sees the copies into one slot are independent of
+    // the reads of another and does not wait for them
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[SLOT];
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // Work order. Workgroup id i runs on XCD i % 8; each (request, kv head)
+    // stream is pinned to XCD stream % 8 and its query tiles take consecutive
+    // slots there, longest (highest) tile first, so the workgroups that share
+    // a stream's K/V run together under one L2.
     const int nrk = p.B * p.Hkv;
-    // longest-first: the highest query tiles (most keys under the causal mask) get the lowest ids
-    const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / nrk);
-    const int rk = blockIdx.x % nrk;
+    const int xcd = (int)(blockIdx.x % kXcds);
+    const int slot_x = (int)(blockIdx.x / kXcds);
+    const int rk = (slot_x / p.n_qtiles) * kXcds + xcd;
+    const int qt = p.n_qtiles - 1 - slot_x % p.n_qtiles;
+    if (rk >= nrk) return;
     const int r = rk / p.Hkv, kh = rk % p.Hkv;
     const int s = blockIdx.y;
     const int g = p.g;
     const int q0 = p.qsl[r];
     const int q_len = p.qsl[r + 1] - q0;
-    const int tpw = kPrefillRows / g;   // tokens per work item
+    const int tpw = ROWS / g;  // tokens per work item
     const int tok0 = qt * tpw;
     if (tok0 >= q_len) return;
     const int L = p.seq_lens ? p.seq_lens[r] : q_len;
@@ -526,24 +567,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(FwdParams p) {
     if (k_begin >= k_end) return;
 
     // this lane's query row
+    const int hsel = lane >> 5;  // which half of the 32-row MFMA tile's k dimension this lane feeds
     const int rho = w * kPrefillRowsPerWave + (lane & 31);
     const int tl = tok0 + rho / g;
     const bool row_ok = rho < tpw * g && tl < q_len;
     const int head = kh * g + rho % g;
     int limit = p.causal ? min(L, ctx + tl + 1) : L;
     limit = row_ok ? min(limit, k_end) : 0;
-    // the wave's key range: [k_begin, wave_max) holds every visible key of its rows;
-    // keys below wave_min are visible to all of them
+    // keys below wave_min are visible to every valid row of the wave: tiles
+    // that end there need no mask (rows past the end of the request are never
+    // stored, so their scores do not matter)
     const int wtok_first = tok0 + (w * kPrefillRowsPerWave) / g;
-    const int wtok_last = min(min(q_len, tok0 + tpw) - 1, tok0 + (w * kPrefillRowsPerWave + 31) / g);
-    const bool wave_any = wtok_first <= wtok_last && w * kPrefillRowsPerWave < tpw * g;
-    const int wave_max = !wave_any ? k_begin : (p.causal ? min(k_end, ctx + wtok_last + 1) : k_end);
+    const bool wave_any = wtok_first < q_len && w * kPrefillRowsPerWave < tpw * g;
     const int wave_min = !wave_any ? k_begin : (p.causal ? min(k_end, ctx + wtok_first + 1) : k_end);
 
     u32x4 qf[KS];
     {
-        const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(q0 + (row_ok ? tl : 0)) * p.H + head) * HD +
-                             (lane >> 5) * 8;
+        const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(q0 + (row_ok ? tl : 0)) * p.H + head) * HD + hsel * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? *(const u32x4*)(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -552,9 +592,48 @@ __global__ __launch_bounds__(256) void prefill_kernel(FwdParams p) {
         sl2 *= *p.k_scale;
         vsc = *p.v_scale;
     }
+
+    // per-lane LDS read offsets; the k-step, key block, output block and key
+    // group parts of each address are immediates
+    // K fragment (kb, ks): tile row kb*32 + (lane & 31), chunk 2 ks + hsel
+    const uint32_t koff = hsel * kChunkPitch + (lane & 31) * 16;
+    // transposed V read (k2, jj, mb): row 16 k2 + 8 jj + 4 hsel + rr,
+    // chunk 4 mb + 2 grp + cc / 2, half cc % 2
+    const uint32_t voff = (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) * kChunkPitch +
+                          (4 * hsel + ((lane & 15) >> 2)) * 16 + (lane & 1) * 8;
+
+    // Tile copies: lane l moves key t0 + l (clamped to the last key, so rows
+    // past the end hold a real, finite key that the mask removes); wave w
+    // moves chunk columns w*CPW .. w*CPW + CPW - 1 of K and of V.
     const int32_t* bt_row = p.bt ? p.bt + (int64_t)r * p.bt_stride : nullptr;
-    const int64_t rstride = (int64_t)p.Hkv * HD;
-    const int64_t hoff = (int64_t)kh * HD;
+    const int64_t rstride = (int64_t)p.Hkv * HD;  // elements per cache row
+    // cache row of this lane's key in the tile starting at t0, in two steps so
+    // the block-table read can be issued an iteration before its use (the
+    // host keeps num_blocks * block_size below 2^31)
+    const int bs_shift = POW2 ? p.bs_shift : -1;
+    auto page_of = [&](int t0) -> int32_t {
+        const int pos = min(t0 + lane, k_end - 1);
+        return bt_row ? bt_row[POW2 ? pos >> bs_shift : pos / p.bs] : 0;
+    };
+    auto row_from = [&](int t0, int32_t page) -> int32_t {
+        const int pos = min(t0 + lane, k_end - 1);
+        return bt_row ? page * p.bs + (POW2 ? pos & (p.bs - 1) : pos % p.bs) : q0 + pos;
+    };
+    using raw_t = u32x2;  // fp8: 8 cached bytes per chunk, widened in registers
+    raw_t st_k[CPW], st_v[CPW];
+    auto issue = [&](const void* cache, int32_t row, uint8_t* slot, raw_t* st) {
+        const uint8_t* src = (const uint8_t*)cache + (((int64_t)row * p.Hkv + kh) * HD + w * CPW * 8) * ESZ;
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            if constexpr (FP8) st[c] = *(const raw_t*)(src + c * 8);
+            else copy16_to_lds<0>(src + c * 16, slot + (w * CPW + c) * kChunkPitch);
+        }
+    };
+    // fp8: widen the staged chunks and store them
+    auto land = [&](uint8_t* slot, const raw_t* st) {
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) *(u32x4*)(slot + (w * CPW + c) * kChunkPitch + lane * 16) = fp8x8_to_bf16x8(st[c]);
+    };
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x16 oacc[MB];
@@ -563,84 +642,163 @@ __global__ __launch_bounds__(256) void prefill_kernel(FwdParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
 
-    // cooperative tile loads: thread -> chunks tid + 256*i
-    u32x4 kreg[LPT], vreg[LPT];
-    auto load_tile = [&](int t0) {
+    // S^T = K Q^T for one tile
+    auto qk = [&](const uint8_t* kslot, f32x16 (&sacc)[KB]) {
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int c = threadIdx.x + 256 * i;
-            const int key = c / CPR;
-            const int rw = kv_row(bt_row, min(t0 + key, L - 1), p.bs, q0);
-            const int64_t e = (int64_t)rw * rstride + hoff + (c % CPR) * 8;
-            kreg[i] = load_kv8<FP8>(p.k_cache, e);
-            vreg[i] = load_kv8<FP8>(p.v_cache, e);
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                sacc[kb] = mfma32x32x16(*(const u32x4*)(kslot + koff + 2 * ks * kChunkPitch + kb * 512), qf[ks], sacc[kb]);
         }
     };
-    load_tile(k_begin);
-    const int hsel = lane >> 5;  // which half of the 32-row MFMA tile's k dimension this lane feeds
-    for (int t0 = k_begin; t0 < k_end; t0 += TILE) {
-        __syncthreads();
+    // causal / length mask of a tile that reaches past wave_min
+    auto mask = [&](int t0, f32x16 (&sacc)[KB]) {
+        if (t0 + TILE > wave_min) {
+            const int lim = limit - t0 - hsel * 4;
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int c = threadIdx.x + 256 * i;
-            *(u32x4*)(k_lds + (c / CPR) * KP + (c % CPR) * 8) = kreg[i];
-            *(u32x4*)(v_lds + (c / CPR) * VP + (c % CPR) * 8) = vreg[i];
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (kb * 32 + (e >> 2) * 8 + (e & 3) >= lim) sacc[kb][e] = -INFINITY;
         }
-        __syncthreads();
-        if (t0 + TILE < k_end) load_tile(t0 + TILE);
-        if (t0 >= wave_max) continue;  // tile entirely in this wave's future: skipped
-
-        f32x16 sacc;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-        const uint16_t* kr = k_lds + (lane & 31) * KP + hsel * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc = mfma32x32x16(*(const u32x4*)(kr + ks * 16), qf[ks], sacc);
-
-        const bool full = t0 + TILE <= wave_min;  // no element of this tile is masked for the wave
-        float sv[16];
+    };
+    // row maximum of a tile (both lane halves hold keys of the same row)
+    auto rowmax = [&](f32x16 (&sacc)[KB]) -> float {
         float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            float x = sacc[e] * sl2;
-            if (!full) {
-                const int kp = t0 + (e >> 2) * 8 + hsel * 4 + (e & 3);
-                x = kp < limit ? x : -INFINITY;
-            }
-            sv[e] = x;
-            mx = fmaxf(mx, x);
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    };
+    // lazy rescale (wave-uniform decision)
+    auto rescale = [&](float mx) {
+        const float m_tile = mx * sl2;  // sl2 > 0: the scaled maximum
+        if (__any(m_tile > m_run + kLazyRescale)) {
+            const float m_new = fmaxf(m_run, m_tile);
+            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < MB; ++i) oacc[i] *= alpha;
+            m_run = m_new;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+    };
+    // probabilities of a tile as bf16 MFMA B operands, and their row sum
+    auto expo = [&](f32x16 (&sacc)[KB], u32x4 (&pf)[2 * KB]) {
+        const float nm = m_run == -INFINITY ? 0.f : -m_run;
         float ps = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            sv[e] = fast_exp2(sv[e] - m_use);
-            ps += sv[e];
+        for (int kb = 0; kb < KB; ++kb) {
+            float pv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                pv[e] = fast_exp2(fmaf(sacc[kb][e], sl2, nm));
+                ps += pv[e];
+            }
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                pf[2 * kb + hf] = u32x4{pack_bf16x2(pv[8 * hf + 0], pv[8 * hf + 1]), pack_bf16x2(pv[8 * hf + 2], pv[8 * hf + 3]),
+                                        pack_bf16x2(pv[8 * hf + 4], pv[8 * hf + 5]), pack_bf16x2(pv[8 * hf + 6], pv[8 * hf + 7])};
         }
-        l_run = l_run * alpha + ps;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < MB; ++i) oacc[i] *= alpha;
-        u32x4 pf[2];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-            pf[k2] = u32x4{pack_bf16x2(sv[8 * k2 + 0], sv[8 * k2 + 1]), pack_bf16x2(sv[8 * k2 + 2], sv[8 * k2 + 3]),
-                           pack_bf16x2(sv[8 * k2 + 4], sv[8 * k2 + 5]), pack_bf16x2(sv[8 * k2 + 6], sv[8 * k2 + 7])};
-        // V^T fragments: lane group (hsel, c) reads keys 16*k2 + 8*jj + 4*hsel + e, columns 16*c + i
-        const int grp_c = (lane >> 4) & 1;
-        const uint16_t* vt = v_lds + (hsel * 4 + ((lane & 15) >> 2)) * VP + grp_c * 16 + (lane & 3) * 4;
+        l_run += ps;
+    };
+    // O^T += V^T P^T for one tile
+    auto pv = [&](const uint8_t* vslot, const u32x4 (&pf)[2 * KB]) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const u32x2 lo = lds_read_tr16(vt + (16 * k2) * VP + mb * 32);
-                const u32x2 hi = lds_read_tr16(vt + (16 * k2 + 8) * VP + mb * 32);
+            for (int k2 = 0; k2 < 2 * KB; ++k2) {
+                const uint8_t* vp = vslot + voff + 4 * mb * kChunkPitch + 16 * k2 * 16;
+                const u32x2 lo = lds_read_tr16(vp);
+                const u32x2 hi = lds_read_tr16(vp + 8 * 16);
                 oacc[mb] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pf[k2], oacc[mb]);
             }
+    };
+
+    // Pipeline, tile i in iteration i. K tile j and V tile j are copied into
+    // slot j % 2: K(i+2) and V(i+1) are issued at the start of iteration i and
+    // land (barrier) at its end, so each copy has a whole iteration to arrive.
+    // Inside the iteration the S^T MFMAs of tile i+1 are issued next to the
+    // exponentials of tile i, and the PV MFMAs of tile i next to the row
+    // maximum of tile i+1, so the matrix cores and the vector ALUs overlap.
+    const int n_tiles = (k_end - k_begin + TILE - 1) / TILE;
+    f32x16 s_a[KB], s_b[KB];
+    float mx;
+    int32_t row_v;  // cache row of this lane's key in tile i+1 (for V(i+1))
+    int32_t pg_k;   // block-table entry of this lane's key in tile i+2 (for K(i+2))
+    {
+        const int32_t row0 = row_from(k_begin, page_of(k_begin));
+        issue(p.k_cache, row0, k_lds0, st_k);
+        issue(p.v_cache, row0, v_lds0, st_v);
+        if constexpr (FP8) {
+            land(k_lds0, st_k);  // (waits for its loads)
+            land(v_lds0, st_v);
+        }
+        row_v = row_from(k_begin + TILE, page_of(k_begin + TILE));
+        if (n_tiles > 1) {
+            issue(p.k_cache, row_v, k_lds1, st_k);
+            if constexpr (FP8) land(k_lds1, st_k);
+        }
+        pg_k = page_of(k_begin + 2 * TILE);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        qk(k_lds0, s_a);
+        mask(k_begin, s_a);
+        mx = rowmax(s_a);
+        __syncthreads();
     }
+    auto iteration = [&](auto par, auto last, int i, f32x16 (&sc)[KB], f32x16 (&sn)[KB]) {
+        constexpr int P = decltype(par)::value;
+        constexpr bool LAST = decltype(last)::value;
+        uint8_t* const k_here = P ? k_lds1 : k_lds0;   // K(i), now free: receives K(i+2)
+        uint8_t* const k_next = P ? k_lds0 : k_lds1;   // K(i+1)
+        uint8_t* const v_here = P ? v_lds1 : v_lds0;   // V(i)
+        uint8_t* const v_next = P ? v_lds0 : v_lds1;   // receives V(i+1)
+        const int t0 = k_begin + i * TILE;
+        const bool load_k = i + 2 < n_tiles;
+        int32_t row_k = 0;
+        if constexpr (!LAST) {
+            if (load_k) {
+                row_k = row_from(t0 + 2 * TILE, pg_k);
+                issue(p.k_cache, row_k, k_here, st_k);
+            }
+            issue(p.v_cache, row_v, v_next, st_v);
+            if (i + 3 < n_tiles) pg_k = page_of(t0 + 3 * TILE);
+        }
+        rescale(mx);
+        u32x4 pf[2 * KB];
+        if constexpr (!LAST) qk(k_next, sn);
+        expo(sc, pf);
+        if constexpr (!LAST) mask(t0 + TILE, sn);
+        pv(v_here, pf);
+        if constexpr (!LAST) {
+            mx = rowmax(sn);
+            if constexpr (FP8) {
+                if (load_k) land(k_here, st_k);
+                land(v_next, st_v);
+            }
+            row_v = row_k;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int i = 0;
+    for (; i + 2 < n_tiles; i += 2) {
+        iteration(I0{}, std::false_type{}, i, s_a, s_b);
+        iteration(I1{}, std::false_type{}, i + 1, s_b, s_a);
+    }
+    if (n_tiles - i == 2) {
+        iteration(I0{}, std::false_type{}, i, s_a, s_b);
+        iteration(I1{}, std::true_type{}, i + 1, s_b, s_a);
+    } else {
+        iteration(I0{}, std::true_type{}, i, s_a, s_b);
+    }
+
     if (!row_ok) return;
     l_run += __shfl_xor(l_run, 32);
     const float inv = l_run > 0.f ? vsc / l_run : 0.f;
@@ -715,7 +873,7 @@ __global__ __launch_bounds__(64) void generic_kernel(FwdParams p) {
     const int64_t rstride = (int64_t)p.Hkv * hd;
     float m = -INFINITY, l = 0.f;
     for (int j = k_begin; j < k_end; ++j) {
-        const int64_t base = (int64_t)kv_row(bt_row, j, p.bs, q0) * rstride + (int64_t)kh * hd;
+        const int64_t base = (int64_t)kv_row(bt_row, j, p.bs, p.bs_shift, q0) * rstride + (int64_t)kh * hd;
         float dot = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1016,9 +1174,17 @@ hipError_t launch_decode(const FwdParams& p, KvType kv, hipStream_t s) {
 
 template <int HD>
 static hipError_t prefill_hd(const FwdParams& p, KvType kv, hipStream_t s) {
-    dim3 grid((unsigned)p.n_qtiles * p.B * p.Hkv, p.num_splits);
-    if (kv == KvType::FP8) hipLaunchKernelGGL((prefill_kernel<HD, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((prefill_kernel<HD, false>), grid, dim3(256), 0, s, p);
+    const int64_t streams_per_xcd = ((int64_t)p.B * p.Hkv + kXcds - 1) / kXcds;
+    dim3 grid((unsigned)(streams_per_xcd * kXcds * p.n_qtiles), p.num_splits);
+    const dim3 block(64 * kPrefillWaves);
+    const bool pow2 = !p.bt || p.bs_shift >= 0;
+    if (kv == KvType::FP8) {
+        if (pow2) hipLaunchKernelGGL((prefill_kernel<HD, true, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((prefill_kernel<HD, true, false>), grid, block, 0, s, p);
+    } else {
+        if (pow2) hipLaunchKernelGGL((prefill_kernel<HD, false, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((prefill_kernel<HD, false, false>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 

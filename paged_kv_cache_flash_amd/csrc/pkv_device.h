@@ -79,15 +79,22 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // memory operations across this point.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Logical position -> (logical block, offset in block). Page sizes that are
+// powers of two (bs_shift >= 0) use a shift and a mask; others divide.
+__device__ __forceinline__ int32_t page_index(int32_t pos, int32_t bs, int32_t bs_shift) {
+    return bs_shift >= 0 ? pos >> bs_shift : pos / bs;
+}
+__device__ __forceinline__ int32_t page_offset(int32_t pos, int32_t bs, int32_t bs_shift) {
+    return bs_shift >= 0 ? pos & (bs - 1) : pos % bs;
+}
+
 // Physical cache row (block * block_size + offset) of logical key `pos`
 // (the host guarantees num_blocks * block_size < 2^31).
 // block_table == nullptr means the flat layout: row = flat_base + pos.
 __device__ __forceinline__ int32_t kv_row(const int32_t* __restrict__ bt_row, int32_t pos, int32_t bs,
-                                          int32_t flat_base) {
+                                          int32_t bs_shift, int32_t flat_base) {
     if (bt_row == nullptr) return flat_base + pos;
-    int32_t blk = pos / bs;
-    int32_t off = pos - blk * bs;
-    return bt_row[blk] * bs + off;
+    return bt_row[page_index(pos, bs, bs_shift)] * bs + page_offset(pos, bs, bs_shift);
 }
 
 }  // namespace pkv

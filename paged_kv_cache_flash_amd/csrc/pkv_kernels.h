@@ -22,6 +22,7 @@ struct FwdParams {
     int64_t bt_stride;
     int64_t T;
     int32_t B, H, Hkv, g, hd, bs;
+    int32_t bs_shift;         // log2(bs) when bs is a power of two, else -1
     int32_t num_splits;       // >= 1
     int32_t split_len;        // keys per split (multiple of the key tile) when num_splits > 1
     int32_t n_qtiles;         // prefill: query tiles per (request, kv head)
@@ -56,10 +57,16 @@ constexpr int kDecodeWaves = 4;
 // and the largest batch whose schedule each wave derives by itself.
 constexpr int kBalancedWaves = 2048;
 constexpr int kBalancedMaxSeqs = 1024;
-// Prefill kernel geometry.
+// Accelerator complex dies of MI355X; consecutive workgroup ids go to
+// consecutive XCDs, each with its own L2.
+constexpr int kXcds = 8;
+// Prefill kernel geometry: four waves of 32 query rows per workgroup sharing
+// K/V tiles of 64 keys in LDS (two workgroups per CU up to head size 128).
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRows = kPrefillRowsPerWave * kPrefillWaves;
-constexpr int kPrefillTile = 32;
+constexpr int prefill_tile(int) { return 64; }
+constexpr int prefill_rows(int) { return kPrefillRowsPerWave * kPrefillWaves; }
+// The largest GQA group the prefill kernel packs (query rows per workgroup).
+constexpr int kPrefillMaxGroup = kPrefillRowsPerWave * kPrefillWaves;
 
 }  // namespace pkv
