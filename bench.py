@@ -34,6 +34,16 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
+# HBM bytes per launch of the dominant kernel, measured with rocprofv3 counters
+# (FETCH_SIZE, WRITE_SIZE) and scaled by the same counters' reading for a plain
+# device copy of known size; each entry carries the hash of the kernel sources
+# it was taken on and is ignored once those sources change.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+KERNEL_SOURCES = ["pkv_attn.hip", "pkv_device.h", "pkv_kernels.h"]
+DOMINANT_KERNEL = {"paged_decode": "decode_balanced_kernel", "chunked_prefill": "prefill_kernel",
+                   "long_decode": "decode_balanced_kernel", "long_decode_cascade": "decode_balanced_kernel",
+                   "fp8_decode": "decode_balanced_kernel"}
+
 WORKLOADS = {
     "paged_decode": "paged decode, 32/8 heads GQA, head 128, bf16, batch 64, ctx U[512,4096], page 16",
     "chunked_prefill": "chunked prefill, batch 8, new U[128,2048] on cached U[0,4096], 32/8 heads, head 128, "
@@ -78,6 +88,55 @@ def kv_bytes(prob, unique=False):
     return toks * per_tok
 
 
+def kernel_sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_flash_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, block_size):
+    """Counter-measured HBM bytes per launch for this workload, or None when
+    no entry was taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = kernel_sources_hash()
+    for ln in open(TRAFFIC_FILE):
+        f = ln.split("#")[0].split()
+        if len(f) == 6 and f[0] == workload and int(f[1]) == block_size and f[5] == want:
+            return int(f[3]) + int(f[4])
+    return None
+
+
+def pmc_summary(args):
+    """Turn rocprofv3 --pmc CSV output into one traffic.txt line: mean
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the dominant kernel, each
+    scaled by true bytes / counter bytes of a plain copy kernel."""
+    import csv
+    import glob
+
+    def mean_counter(d, counter, name):
+        vals = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] == counter and name in row["Kernel_Name"]:
+                    vals.append(float(row["Counter_Value"]))
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {name} under {d}")
+        return sum(vals) / len(vals)
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.pmc_summary
+    copy_bytes = args.calibrate_bytes
+    f_fac = copy_bytes / (1024 * mean_counter(cfetch_dir, "FETCH_SIZE", "copyBuffer"))
+    w_fac = copy_bytes / (1024 * mean_counter(cwrite_dir, "WRITE_SIZE", "copyBuffer"))
+    kern = DOMINANT_KERNEL[args.workload]
+    fetch = mean_counter(fetch_dir, "FETCH_SIZE", kern) * 1024 * f_fac
+    write = mean_counter(write_dir, "WRITE_SIZE", kern) * 1024 * w_fac
+    print(f"{args.workload} {args.block_size} {kern} {int(round(fetch))} {int(round(write))} {kernel_sources_hash()}"
+          f"  # copy factors fetch {f_fac:.4f} write {w_fac:.4f}")
+
+
 def visible_flops(prob):
     """4 * hd * H * (visible query-key pairs): QK^T and PV, causal pairs only."""
     ql = prob.q_lens.astype(np.int64)
@@ -104,8 +163,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="only summarise rocprofv3 --pmc output of this workload into a traffic line")
+    ap.add_argument("--calibrate-bytes", type=int, default=1 << 30, help="bytes of the copy in the calibration runs")
     args = ap.parse_args()
 
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.calibrate_copy:
         import torch
         n = args.calibrate_copy << 20
@@ -232,6 +297,9 @@ def main():
         f"merge {merge_ms / max(calls, 1):.4f} ms avg")
 
     decode_like = args.workload != "chunked_prefill"
+    # HBM bytes per launch of the dominant kernel from committed counter runs
+    # (None unless they were taken on the current kernel sources)
+    traffic = measured_traffic(args.workload, prob.bs)
     if decode_like:
         kvb = kv_bytes(prob, unique=cascade)
         value = kvb / (ms_step * 1e-3) / 1e9
@@ -240,14 +308,16 @@ def main():
         # whole KV once (cascade: a prefix launch and a suffix launch per step)
         achieved = kvb / (main_ms / args.steps * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "algorithmic_bytes_per_launch": kvb}
     else:
         fl = visible_flops(prob)
         value = fl / (ms_step * 1e-3) / 1e12
         metric, unit = "causal prefill TFLOP/s", "TFLOP/s"
         achieved = fl / (main_ms / args.steps * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                    "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                    "algorithmic_flops_per_launch": fl}
 
     cpu = None
     if not args.no_cpu_baseline:
