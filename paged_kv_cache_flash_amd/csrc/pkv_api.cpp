@@ -104,6 +104,13 @@ pkv_status validate_sizes(const pkv_varlen_args* a) {
     return ok();
 }
 
+// Waves of the balanced decode grid: one workgroup per CU for bf16 caches;
+// fp8 tiles carry half the bytes, so two workgroups per CU keep as many bytes
+// in flight (where their LDS fits: head size up to 128).
+static int64_t balanced_waves(const pkv_varlen_args* a) {
+    return a->kv_dtype == PKV_FP8_E4M3FN && a->head_size <= 128 ? 2 * kBalancedWaves : kBalancedWaves;
+}
+
 Plan make_plan(const pkv_varlen_args* a) {
     Plan pl{};
     const int g = a->num_heads / a->num_kv_heads;
@@ -114,11 +121,11 @@ Plan make_plan(const pkv_varlen_args* a) {
     int align;
     if (mfma && (int64_t)a->max_seqlen_q * g <= kDecodeRows && a->num_splits == 0 &&
         a->num_seqs <= kBalancedMaxSeqs) {
-        // balanced decode: kBalancedWaves waves share the KV tiles equally
+        // balanced decode: balanced_waves() waves share the KV tiles equally
         pl.kind = Kind::DecodeBalanced;
-        pl.splits = kBalancedWaves;
+        pl.splits = (int32_t)balanced_waves(a);
         pl.split_len = kDecodeTile;
-        const int64_t slots = kBalancedWaves + (int64_t)a->num_seqs * a->num_kv_heads;
+        const int64_t slots = balanced_waves(a) + (int64_t)a->num_seqs * a->num_kv_heads;
         pl.workspace = (size_t)slots * kDecodeRows * (a->head_size + 1) * sizeof(float) +
                        (size_t)(a->num_seqs + 1) * sizeof(int32_t);
         return pl;
@@ -245,8 +252,8 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     p.causal = a->causal ? 1 : 0;
     p.scale_log2 = a->softmax_scale * 1.4426950408889634f;  // log2(e): kernels use exp2
     if (pl.kind == Kind::DecodeBalanced) {
-        const int64_t slots = kBalancedWaves + (int64_t)a->num_seqs * a->num_kv_heads;
-        p.sk_waves = kBalancedWaves;
+        const int64_t slots = balanced_waves(a) + (int64_t)a->num_seqs * a->num_kv_heads;
+        p.sk_waves = (int32_t)balanced_waves(a);
         p.part_o = (float*)a->workspace;
         p.part_lse = p.part_o + (size_t)slots * kDecodeRows * a->head_size;
         p.sk_prefix = (int32_t*)(p.part_lse + (size_t)slots * kDecodeRows);

@@ -98,110 +98,90 @@ __device__ __forceinline__ int request_of(const int32_t* qsl, int B, int64_t tok
 
 // ----------------------------------------------------------------- decode
 
-// One wave's share of a decode work item: keys [k_first, k_end) of request r,
-// kv head kh, taken in 32-key tiles k_first, k_first + step, ... (step is a
-// multiple of 32). The item's query rows (q_len tokens x g heads of the group,
-// at most 16) are the columns of 16x16x32 MFMAs: S^T = K Q^T, O^T += V^T P^T.
-// Returns the wave's online-softmax state: m (log2 domain, row-uniform),
-// l (per lane: the sum over this lane's keys), and O^T (lane holds rows
-// l%16, head-dim elements 16*mb + 4*(l/16) + i).
-template <int HD, bool FP8, bool PAGED>
-__device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* vl, int lane, int r, int kh, int q0,
-                                             int q_len, int L, int k_first, int step, int k_end, float& m_run,
-                                             float& l_run, f32x4 (&oacc)[HD / 16]) {
-    constexpr int TILE = kDecodeTile;
-    constexpr int KS = HD / 32;             // k-steps of S^T = K Q^T
-    constexpr int MB = HD / 16;             // 16-row blocks of O^T
-    constexpr int VP = HD + 16;             // LDS pitch of a V row (bf16 elements)
-    constexpr int CPR = HD / 8;             // 16-byte chunks per row
-    constexpr int VLOADS = TILE * CPR / 64; // V chunks per lane per tile
-    static_assert(HD % 32 == 0 && VLOADS >= 1, "");
+// One decode wave's 32-key tile: loads, LDS staging and compute. The LDS area
+// of a wave holds the tile's K and V row-major in bf16. The K pitch (HD + 8
+// elements) puts consecutive rows 16 bytes apart in bank space, so the
+// 16-byte A-operand reads of 8 consecutive rows hit 32 distinct banks; the V
+// pitch (HD + 16) does the same for the transposed 8-byte reads.
+template <int HD, bool FP8>
+struct DecodeTile {
+    static constexpr int TILE = kDecodeTile;
+    static constexpr int KS = HD / 32;         // k-steps of S^T = K Q^T
+    static constexpr int MB = HD / 16;         // 16-row blocks of O^T
+    static constexpr int KP = HD + 8;
+    static constexpr int VP = HD + 16;
+    static constexpr int K_ELEMS = TILE * KP;
+    static constexpr int ELEMS = TILE * (KP + VP);  // bf16 elements per wave
+    static constexpr int ESZ = FP8 ? 1 : 2;    // bytes per cached element
+    static constexpr int EPL = 16 / ESZ;       // elements per 16-byte load
+    static constexpr int GPR = HD / EPL;       // 16-byte loads per cache row (one kv head)
+    static constexpr int NL = TILE * GPR / 64; // loads per lane per tile, for K and again for V
+    static_assert(HD % 32 == 0 && 64 % GPR == 0 && NL >= 1, "");
 
-    const int ctx = L - q_len;
-    const int g = p.g;
-    const int row = lane & 15;
-    const int G = lane >> 4;
-    const int rows_total = q_len * g;
-    const bool row_ok = row < rows_total;
-    const int tl = row_ok ? row / g : 0;
-    const int hh = kh * g + (row_ok ? row % g : 0);
-    int limit = p.causal ? min(L, ctx + tl + 1) : L;
-    limit = row_ok ? min(limit, k_end) : 0;
+    static constexpr int KPL = 64 / GPR;       // keys per load instruction
 
-    u32x4 qf[KS];
-    {
-        const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(q0 + tl) * p.H + hh) * HD + G * 8;
+    // Key (within the tile) that load i of `lane` reads.
+    static __device__ __forceinline__ int key_of(int lane, int i) { return lane / GPR + KPL * i; }
+
+    // K and V of a tile with row-coalesced 16-byte loads: load i of lane l
+    // covers granule c = l + 64 i, i.e. key c / GPR, elements (c % GPR) * EPL
+    // onward, so each group of GPR consecutive lanes reads one whole cache row
+    // of the kv head. (Reading K in the MFMA operand layout instead, 16 keys x
+    // 64 bytes per instruction, streams far below the HBM rate.) rows[i] is
+    // the cache row of key key_of(lane, i); every lane translates its own
+    // keys, so issuing the loads needs no cross-lane traffic.
+    static __device__ __forceinline__ void load(const FwdParams& p, int lane, const int (&rows)[NL], int kh,
+                                                u32x4 (&kr)[NL], u32x4 (&vr)[NL]) {
+        const int64_t rstride = (int64_t)p.Hkv * HD;
+        const int64_t col = (int64_t)kh * HD + (lane % GPR) * EPL;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < NL; ++i) {
+            const int64_t e = (int64_t)rows[i] * rstride + col;
+            kr[i] = *(const u32x4*)((const uint8_t*)p.k_cache + e * ESZ);
+            vr[i] = *(const u32x4*)((const uint8_t*)p.v_cache + e * ESZ);
+        }
     }
-    float sl2 = p.scale_log2;
-    if constexpr (FP8) sl2 *= *p.k_scale;
-    const int32_t* bt_row = PAGED ? p.bt + (int64_t)r * p.bt_stride : nullptr;
-    const int64_t rstride = (int64_t)p.Hkv * HD;
-    const int64_t hoff = (int64_t)kh * HD;
-
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int i = 0; i < MB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Address translation is split in two so that the block-table load of a
-    // tile can be issued a full tile ahead of its use: page_for issues the
-    // load of the block-table entry for the key this lane translates in tile t
-    // (lanes 32..63 repeat 0..31), row_from turns it into a cache row when the
-    // tile's loads are issued. (Using the entry right after loading it would
-    // make the wave wait for every load in flight, since loads retire in
-    // order.) Keys at or past the end of the range are clamped to its last
-    // key, so a prefetch past the end re-reads one cached row and every
-    // address stays inside the request's pages.
-    auto page_for = [&](int t) {
-        const int pos = min(t + (lane & 31), k_end - 1);
-        if constexpr (PAGED) return bt_row[page_index(pos, p.bs, p.bs_shift)];
-        else return q0 + pos;
-    };
-    auto row_from = [&](int t, int page) {
-        const int pos = min(t + (lane & 31), k_end - 1);
-        if constexpr (PAGED) return page * p.bs + page_offset(pos, p.bs, p.bs_shift);
-        else return page;
-    };
-    using raw_t = raw8_t<FP8>;
-    // K straight into MFMA A-operand registers, V as row-major 16-byte chunks
-    // for the LDS transpose.
-    auto load_tile = [&](int my_row, raw_t (&kf)[2][KS], raw_t (&vv)[VLOADS]) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int rb = __shfl(my_row, b * 16 + row);
-            const int64_t e0 = (int64_t)rb * rstride + hoff + G * 8;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kf[b][ks] = load_raw8<FP8>(p.k_cache, e0 + ks * 32);
-        }
-#pragma unroll
-        for (int i = 0; i < VLOADS; ++i) {
-            const int c = lane + 64 * i;
-            const int rv = __shfl(my_row, c / CPR);
-            vv[i] = load_raw8<FP8>(p.v_cache, (int64_t)rv * rstride + hoff + (c % CPR) * 8);
-        }
-    };
-    // V of a tile: registers -> LDS, row-major (read back transposed)
-    auto store_v = [&](const raw_t (&vv)[VLOADS]) {
+    // registers -> LDS, row-major bf16 (fp8 widened, exactly)
+    static __device__ __forceinline__ void store(uint16_t* stage, int lane, const u32x4 (&kr)[NL],
+                                                 const u32x4 (&vr)[NL]) {
+        uint16_t* const kl = stage;
+        uint16_t* const vl = stage + K_ELEMS;
         wave_lds_sync();
 #pragma unroll
-        for (int i = 0; i < VLOADS; ++i) {
+        for (int i = 0; i < NL; ++i) {
             const int c = lane + 64 * i;
-            *(u32x4*)(vl + (c / CPR) * VP + (c % CPR) * 8) = to_bf16x8<FP8>(vv[i]);
+            const int key = c / GPR, col = (c % GPR) * EPL;
+            if constexpr (FP8) {
+                *(u32x4*)(kl + key * KP + col) = fp8x8_to_bf16x8(u32x2{kr[i].x, kr[i].y});
+                *(u32x4*)(kl + key * KP + col + 8) = fp8x8_to_bf16x8(u32x2{kr[i].z, kr[i].w});
+                *(u32x4*)(vl + key * VP + col) = fp8x8_to_bf16x8(u32x2{vr[i].x, vr[i].y});
+                *(u32x4*)(vl + key * VP + col + 8) = fp8x8_to_bf16x8(u32x2{vr[i].z, vr[i].w});
+            } else {
+                *(u32x4*)(kl + key * KP + col) = kr[i];
+                *(u32x4*)(vl + key * VP + col) = vr[i];
+            }
         }
         wave_lds_sync();
-    };
-    // One tile: S^T from K in registers, online softmax, O^T += V^T P^T with
-    // V^T read transposed from LDS.
-    auto compute_tile = [&](int t0, const raw_t (&kf)[2][KS]) {
-        // S^T[key][row] for two 16-key blocks
+    }
+    // One tile from LDS: S^T with K as the A operand and the item's query
+    // rows as the 16 columns, masking keys at or past `limit` (per row),
+    // online softmax, then O^T += V^T P^T with V^T read transposed. m_run is
+    // row-uniform (log2 domain), l_run per lane (this lane's keys only).
+    static __device__ __forceinline__ void compute(const uint16_t* stage, int lane, int t0, int limit, float sl2,
+                                                   const u32x4 (&qf)[KS], float& m_run, float& l_run,
+                                                   f32x4 (&oacc)[MB]) {
+        const uint16_t* const kl = stage;
+        const uint16_t* const vl = stage + K_ELEMS;
+        const int row = lane & 15;
+        const int G = lane >> 4;
         f32x4 sacc[2];
+        const uint16_t* kp = kl + row * KP + G * 8;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             sacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sacc[b] = mfma16x16x32(to_bf16x8<FP8>(kf[b][ks]), qf[ks], sacc[b]);
+            for (int ks = 0; ks < KS; ++ks)
+                sacc[b] = mfma16x16x32(*(const u32x4*)(kp + b * 16 * KP + ks * 32), qf[ks], sacc[b]);
         }
         float sv[8];
         float mx = -INFINITY;
@@ -209,8 +189,8 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* vl, i
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int kp = t0 + b * 16 + G * 4 + i;
-                const float x = kp < limit ? sacc[b][i] * sl2 : -INFINITY;
+                const int key = t0 + b * 16 + G * 4 + i;
+                const float x = key < limit ? sacc[b][i] * sl2 : -INFINITY;
                 sv[b * 4 + i] = x;
                 mx = fmaxf(mx, x);
             }
@@ -239,43 +219,111 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* vl, i
             const u32x2 hi = lds_read_tr16(vt + 16 * VP + mb * 16);
             oacc[mb] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, oacc[mb]);
         }
+    }
+};
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 and leaves
+// the other counters alone.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Query fragment of a decode item: lane l feeds row l % 16 (token row / g,
+// head kh * g + row % g), head-dim elements 8 * (l / 16) + 32 ks onward.
+template <int HD>
+__device__ __forceinline__ void load_decode_q(const FwdParams& p, int lane, int q0, int rows_total, int kh,
+                                              u32x4 (&qf)[HD / 32]) {
+    const int row = lane & 15;
+    const bool row_ok = row < rows_total;
+    const int tl = row_ok ? row / p.g : 0;
+    const int hh = kh * p.g + (row_ok ? row % p.g : 0);
+    const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(q0 + tl) * p.H + hh) * HD + (lane >> 4) * 8;
+#pragma unroll
+    for (int ks = 0; ks < HD / 32; ++ks) qf[ks] = row_ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Largest key index + 1 that query row (lane % 16) of an item may see.
+__device__ __forceinline__ int decode_row_limit(const FwdParams& p, int lane, int q_len, int L) {
+    const int row = lane & 15;
+    if (row >= q_len * p.g) return 0;
+    return p.causal ? min(L, L - q_len + row / p.g + 1) : L;
+}
+
+// One wave's share of a decode work item: keys [k_first, k_end) of request r,
+// kv head kh, taken in 32-key tiles k_first, k_first + step, ... (step is a
+// multiple of 32). The item's query rows (q_len tokens x g heads of the group,
+// at most 16) are the columns of 16x16x32 MFMAs: S^T = K Q^T, O^T += V^T P^T.
+// `stage` is the wave's LDS area. Returns the wave's online-softmax state: m
+// (log2 domain, row-uniform), l (summed over the row), and O^T (lane holds
+// row l%16, head-dim elements 16*mb + 4*(l/16) + i).
+template <int HD, bool FP8, bool PAGED>
+__device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage, int lane, int r, int kh, int q0,
+                                             int q_len, int L, int k_first, int step, int k_end, float& m_run,
+                                             float& l_run, f32x4 (&oacc)[HD / 16]) {
+    using DT = DecodeTile<HD, FP8>;
+    constexpr int NL = DT::NL;
+    u32x4 qf[DT::KS];
+    load_decode_q<HD>(p, lane, q0, q_len * p.g, kh, qf);
+    const int limit = min(decode_row_limit(p, lane, q_len, L), k_end);
+    float sl2 = p.scale_log2;
+    if constexpr (FP8) sl2 *= *p.k_scale;
+    const int32_t* bt_row = PAGED ? p.bt + (int64_t)r * p.bt_stride : nullptr;
+
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int i = 0; i < DT::MB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Address translation is split in two so that the block-table loads of a
+    // tile can be issued a full tile ahead of their use: page_for issues the
+    // loads of the block-table entries of the keys this lane will read in
+    // tile t, row_from turns them into cache rows when the tile's loads are
+    // issued. (Using an entry right after loading it would make the wave wait
+    // for every load in flight, since loads retire in order.) Keys at or past
+    // the end of the range are clamped to its last key, so a prefetch past
+    // the end re-reads one cached row and every address stays inside the
+    // request's pages.
+    auto page_for = [&](int t, int (&pg)[NL]) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int pos = min(t + DT::key_of(lane, i), k_end - 1);
+            if constexpr (PAGED) pg[i] = bt_row[page_index(pos, p.bs, p.bs_shift)];
+            else pg[i] = q0 + pos;
+        }
+    };
+    auto row_from = [&](int t, const int (&pg)[NL], int (&rows)[NL]) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int pos = min(t + DT::key_of(lane, i), k_end - 1);
+            if constexpr (PAGED) rows[i] = pg[i] * p.bs + page_offset(pos, p.bs, p.bs_shift);
+            else rows[i] = pg[i];
+        }
     };
 
     // Software pipeline over the wave's tiles. Iteration i: request the
-    // block-table entry of tile i+2, issue the K/V loads of tile i+1
+    // block-table entries of tile i+2, issue the K/V loads of tile i+1
     // (unconditionally: past the end they re-read a cached row), compute tile
-    // i (K in registers, V already in LDS), turn the block-table entry into a
-    // row index, and move tile i+1's V into LDS. K is double-buffered in
-    // registers, V single-buffered (it leaves the registers each iteration).
-    // Every load result is consumed in the iteration that issued it, so the
-    // wait before a compute covers the current tile only.
+    // i from LDS, turn the block-table entries into row indices, and move tile
+    // i+1 into LDS. Every load result is consumed in the iteration that
+    // issued it, so the wait before the LDS stores covers that tile only.
     int t_cur = k_first;
     if (t_cur < k_end) {
-        raw_t ka[2][KS], kb[2][KS], vv[VLOADS];
-        const int row0 = row_from(t_cur, page_for(t_cur));
-        const int pg1 = page_for(t_cur + step);
-        load_tile(row0, ka, vv);
-        int row1 = row_from(t_cur + step, pg1);
-        store_v(vv);
+        u32x4 kr[NL], vr[NL];
+        int pg[NL], rows[NL];
+        page_for(t_cur, pg);
+        row_from(t_cur, pg, rows);
+        page_for(t_cur + step, pg);
+        DT::load(p, lane, rows, kh, kr, vr);
+        row_from(t_cur + step, pg, rows);
+        DT::store(stage, lane, kr, vr);
         while (true) {
-            int pg2 = page_for(t_cur + 2 * step);
-            load_tile(row1, kb, vv);
+            page_for(t_cur + 2 * step, pg);
+            DT::load(p, lane, rows, kh, kr, vr);
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
-            compute_tile(t_cur, ka);
-            row1 = row_from(t_cur + 2 * step, pg2);
-            store_v(vv);
-            __builtin_amdgcn_sched_barrier(0);
+            DT::compute(stage, lane, t_cur, limit, sl2, qf, m_run, l_run, oacc);
+            row_from(t_cur + 2 * step, pg, rows);
             t_cur += step;
             if (t_cur >= k_end) break;
-            pg2 = page_for(t_cur + 2 * step);
-            load_tile(row1, ka, vv);
+            DT::store(stage, lane, kr, vr);
             __builtin_amdgcn_sched_barrier(0);
-            compute_tile(t_cur, kb);
-            row1 = row_from(t_cur + 2 * step, pg2);
-            store_v(vv);
-            __builtin_amdgcn_sched_barrier(0);
-            t_cur += step;
-            if (t_cur >= k_end) break;
         }
     }
     // per-row sum over the four lane groups
@@ -290,14 +338,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
     constexpr int TILE = kDecodeTile;
     constexpr int NW = kDecodeWaves;
     constexpr int MB = HD / 16;
-    constexpr int VP = HD + 16;
-    constexpr int VSM = NW * TILE * VP;     // bf16 elements of V staging
-    constexpr int OSM = NW * 16 * HD * 2;   // the same bytes reused as fp32 partial outputs
+    constexpr int VSM = NW * DecodeTile<HD, FP8>::ELEMS;  // bf16 elements of K/V staging
+    constexpr int OSM = NW * 16 * HD * 2;           // the same bytes reused as fp32 partial outputs
     __shared__ __attribute__((aligned(16))) uint16_t smem[VSM > OSM ? VSM : OSM];
     __shared__ float sm_m[NW][16], sm_l[NW][16];
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
     const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
     const int q0 = p.qsl[r];
     const int q_len = p.qsl[r + 1] - q0;
@@ -309,7 +356,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
 
     float m_run, l_run;
     f32x4 oacc[MB];
-    decode_range<HD, FP8, PAGED>(p, smem + w * TILE * VP, lane, r, kh, q0, q_len, L, k_begin + w * TILE, NW * TILE,
+    decode_range<HD, FP8, PAGED>(p, smem + w * DecodeTile<HD, FP8>::ELEMS, lane, r, kh, q0, q_len, L, k_begin + w * TILE,
+                                 NW * TILE,
                                  k_end, m_run, l_run, oacc);
     const int row = lane & 15;
     const int G = lane >> 4;
@@ -385,14 +433,25 @@ __device__ __forceinline__ int decode_tiles_of(const FwdParams& p, int r) {
 // Wave index whose tile range holds global tile t (ranges [w N / W, (w+1) N / W)).
 __device__ __forceinline__ int64_t wave_of_tile(int64_t t, int64_t N, int64_t W) { return ((t + 1) * W - 1) / N; }
 
+// Position of a decode wave in the global tile list: request r, kv head kh,
+// tile t of the (r, kh) item, global index T, with request r's tiles per
+// item (n), KV length (L) and query range (q0, q_len). An invalid cursor
+// (past the wave's range) keeps pointing at the wave's last tile.
+struct DecodeCursor {
+    int64_t T;
+    int r, kh, t, n, L, q0, q_len;
+    bool valid;
+};
+
 template <int HD, bool FP8, bool PAGED>
 __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel(FwdParams p) {
+    using DT = DecodeTile<HD, FP8>;
     constexpr int TILE = kDecodeTile;
-    constexpr int MB = HD / 16;
-    constexpr int VP = HD + 16;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE * VP];
+    constexpr int MB = DT::MB;
+    constexpr int NL = DT::NL;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * DT::ELEMS];
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
     const int64_t gw = (int64_t)blockIdx.x * 4 + w;
     const int64_t W = (int64_t)gridDim.x * 4;
 
@@ -403,8 +462,10 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
         int n = base + lane < p.B ? decode_tiles_of(p, base + lane) : 0;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
-        total += n;
+        total += __builtin_amdgcn_readfirstlane(n);
     }
+    // (the scan results are the same in every lane; readfirstlane tells the
+    // compiler so, which keeps the schedule and the loop below scalar)
     const int64_t N = (int64_t)p.Hkv * total;
     const int64_t T0 = gw * N / W, T1 = (gw + 1) * N / W;
     int r = -1, pr = 0, carry = 0;
@@ -424,39 +485,119 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
         if (bal != 0 && r < 0) {
             const int src = __ffsll((unsigned long long)bal) - 1;
             r = base + src;
-            pr = __shfl(excl, src);
+            pr = __builtin_amdgcn_readfirstlane(__shfl(excl, src));
         }
-        carry += __shfl(incl, 63);
+        carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
     }
     if (gw == 0 && lane == 0) p.sk_prefix[p.B] = carry;
     if (T0 >= T1 || r < 0) return;
 
-    int n_r = decode_tiles_of(p, r);
-    const int64_t off = T0 - (int64_t)p.Hkv * pr;
-    int kh = (int)(off / n_r);
-    int t = (int)(off % n_r);
-    int64_t T = T0;
-    uint16_t* vl = smem + w * TILE * VP;
+    // Request metadata window: lane j describes request wb + j.
+    int wb = -1, w_n = 0, w_L = 0, w_q0 = 0, w_ql = 0;
+    auto fill = [&](DecodeCursor& c) {
+        if (wb < 0 || c.r >= wb + 64) {
+            wb = c.r;
+            const int x = wb + lane;
+            w_q0 = x < p.B ? p.qsl[x] : 0;
+            w_ql = x < p.B ? p.qsl[x + 1] - w_q0 : 0;
+            w_L = x < p.B ? (p.seq_lens ? p.seq_lens[x] : w_ql) : 0;
+            w_n = w_ql > 0 ? (w_L + TILE - 1) / TILE : 0;
+        }
+        const int j = __builtin_amdgcn_readfirstlane(c.r - wb);
+        c.n = __builtin_amdgcn_readlane(w_n, j);
+        c.L = __builtin_amdgcn_readlane(w_L, j);
+        c.q0 = __builtin_amdgcn_readlane(w_q0, j);
+        c.q_len = __builtin_amdgcn_readlane(w_ql, j);
+    };
+    // next tile of the wave's range (request-major, then kv head)
+    auto advance = [&](DecodeCursor& c) {
+        if (!c.valid) return;
+        if (c.T + 1 >= T1) {
+            c.valid = false;
+            return;
+        }
+        const DecodeCursor prev = c;
+        ++c.T;
+        if (++c.t == c.n) {
+            c.t = 0;
+            if (++c.kh == p.Hkv) {
+                c.kh = 0;
+                do {
+                    ++c.r;
+                    fill(c);
+                } while (c.n == 0 && c.r < p.B);
+                if (c.r >= p.B) {  // only on metadata that contradicts itself
+                    c = prev;
+                    c.valid = false;
+                }
+            }
+        }
+    };
+
+    DecodeCursor c0;
+    c0.r = r;
+    fill(c0);
+    {
+        const int64_t off = T0 - (int64_t)p.Hkv * pr;
+        c0.kh = (int)(off / c0.n);
+        c0.t = (int)(off % c0.n);
+    }
+    c0.T = T0;
+    c0.valid = true;
+    DecodeCursor c1 = c0;
+    advance(c1);
+    DecodeCursor c2 = c1;
+    advance(c2);
+
+    // Keys are clamped to the request's last key, so tiles that run past it
+    // (and the re-read of the last tile past the wave's range) stay inside
+    // the request's pages. Each lane translates the keys it loads itself.
+    auto page_for = [&](const DecodeCursor& c, int (&pg)[NL]) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int pos = min(c.t * TILE + DT::key_of(lane, i), c.L - 1);
+            if constexpr (PAGED) pg[i] = p.bt[(int64_t)c.r * p.bt_stride + page_index(pos, p.bs, p.bs_shift)];
+            else pg[i] = c.q0 + pos;
+        }
+    };
+    auto row_from = [&](const DecodeCursor& c, const int (&pg)[NL], int (&rows)[NL]) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int pos = min(c.t * TILE + DT::key_of(lane, i), c.L - 1);
+            if constexpr (PAGED) rows[i] = pg[i] * p.bs + page_offset(pos, p.bs, p.bs_shift);
+            else rows[i] = pg[i];
+        }
+    };
+
+    uint16_t* const stage = smem + w * DT::ELEMS;
+    float sl2 = p.scale_log2;
+    if constexpr (FP8) sl2 *= *p.k_scale;
+    const float vsc = FP8 ? *p.v_scale : 1.f;
     const int row = lane & 15;
     const int G = lane >> 4;
-    const float vsc = FP8 ? *p.v_scale : 1.f;
-    while (true) {
-        const int cnt = (int)min((int64_t)(n_r - t), T1 - T);
-        const int q0 = p.qsl[r];
-        const int q_len = p.qsl[r + 1] - q0;
-        const int L = p.seq_lens ? p.seq_lens[r] : q_len;
-        const int k_end = min(L, (t + cnt) * TILE);
-        float m_run, l_run;
-        f32x4 oacc[MB];
-        decode_range<HD, FP8, PAGED>(p, vl, lane, r, kh, q0, q_len, L, t * TILE, TILE, k_end, m_run, l_run, oacc);
-        const int rows_total = q_len * p.g;
-        if (row < rows_total) {
-            const float inv = l_run > 0.f ? vsc / l_run : 0.f;
+
+    u32x4 qf[DT::KS], qn[DT::KS];
+    load_decode_q<HD>(p, lane, c0.q0, c0.q_len * p.g, c0.kh, qf);
+    int limit = decode_row_limit(p, lane, c0.q_len, c0.L);
+    int seg_t0 = c0.t;  // first tile of the current item segment
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 oacc[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The end of an item segment: the final output when the segment is the
+    // whole item, else a partial state in slot (wave + item).
+    auto finish = [&](const DecodeCursor& c) {
+        float l = l_run;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (row < c.q_len * p.g) {
+            const float inv = l > 0.f ? vsc / l : 0.f;
             const float mu = m_run == -INFINITY ? 0.f : m_run;
-            const float lse = l_run > 0.f ? (mu + fast_log2(l_run)) * kLn2 : -INFINITY;
-            if (t == 0 && cnt == n_r) {  // the whole item: final output
-                const int64_t tok = q0 + row / p.g;
-                const int head = kh * p.g + row % p.g;
+            const float lse = l > 0.f ? (mu + fast_log2(l)) * kLn2 : -INFINITY;
+            if (seg_t0 == 0 && c.t == c.n - 1) {
+                const int64_t tok = c.q0 + row / p.g;
+                const int head = c.kh * p.g + row % p.g;
                 uint16_t* op = (uint16_t*)p.out + (tok * p.H + head) * HD + G * 4;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
@@ -464,28 +605,61 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
                     store_bf16<4>(op + mb * 16, v4);
                 }
                 if (p.lse && G == 0) p.lse[(int64_t)head * p.T + tok] = lse;
-            } else {  // a segment: partial state into slot (wave + item)
-                const int64_t slot = gw + (int64_t)r * p.Hkv + kh;
+            } else {
+                const int64_t slot = gw + (int64_t)c.r * p.Hkv + c.kh;
                 float* op = p.part_o + (slot * 16 + row) * HD + G * 4;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) *(f32x4*)(op + mb * 16) = oacc[mb] * inv;
                 if (G == 0) p.part_lse[slot * 16 + row] = lse;
             }
         }
-        T += cnt;
-        if (T >= T1) break;
-        t += cnt;
-        if (t == n_r) {
-            t = 0;
-            if (++kh == p.Hkv) {
-                kh = 0;
-                do {
-                    ++r;
-                    n_r = r < p.B ? decode_tiles_of(p, r) : 1;
-                } while (n_r == 0);
-                if (r >= p.B) break;  // only on metadata that contradicts itself
-            }
+        m_run = -INFINITY;
+        l_run = 0.f;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    // One software pipeline over the wave's whole tile range, across item
+    // boundaries: iteration i requests the block-table entries of tile i+2,
+    // issues the K/V loads of tile i+1 (and, when tile i+1 opens another
+    // item, that item's query fragment), computes tile i from LDS, closes
+    // tile i's item segment if it ends there, and moves tile i+1 into LDS.
+    // A new item therefore costs no pipeline restart. Past the wave's range
+    // the last tile is re-read (cached) and never computed.
+    u32x4 kr[NL], vr[NL];
+    int pg[NL], rows[NL];
+    page_for(c0, pg);
+    row_from(c0, pg, rows);
+    page_for(c1, pg);
+    DT::load(p, lane, rows, c0.kh, kr, vr);
+    row_from(c1, pg, rows);
+    DT::store(stage, lane, kr, vr);
+    while (true) {
+        page_for(c2, pg);
+        DT::load(p, lane, rows, c1.kh, kr, vr);
+        const bool c1_new = c1.valid && c1.t == 0;
+        if (c1_new) load_decode_q<HD>(p, lane, c1.q0, c1.q_len * p.g, c1.kh, qn);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
+        DT::compute(stage, lane, c0.t * TILE, limit, sl2, qf, m_run, l_run, oacc);
+        if (!c1.valid || c1_new) finish(c0);
+        if (!c1.valid) break;
+        row_from(c2, pg, rows);
+        c0 = c1;
+        c1 = c2;
+        advance(c2);
+        if (c1_new) {
+#pragma unroll
+            for (int ks = 0; ks < DT::KS; ++ks) qf[ks] = qn[ks];
+            limit = decode_row_limit(p, lane, c0.q_len, c0.L);
+            seg_t0 = 0;
         }
+        DT::store(stage, lane, kr, vr);
+        // Nothing may be left in flight here: the next iteration's loads are
+        // then the only ones its waits count (the output stores of a finished
+        // segment and the query loads would otherwise make the compiler wait
+        // on every tile load it issues).
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 

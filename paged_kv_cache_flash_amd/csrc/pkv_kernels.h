@@ -53,9 +53,12 @@ hipError_t launch_cache_write(const void* key, const void* value, int src_f32, v
 constexpr int kDecodeRows = 16;
 constexpr int kDecodeTile = 32;
 constexpr int kDecodeWaves = 4;
-// Balanced decode: waves in the grid (256 CUs x 8 resident waves on MI355X)
-// and the largest batch whose schedule each wave derives by itself.
-constexpr int kBalancedWaves = 2048;
+// Balanced decode: waves in the grid for a bf16 cache (one workgroup of 4
+// waves on each of the 256 CUs of MI355X; twice as many waves, all resident,
+// stream the paged KV slightly slower, so the memory system is past
+// saturation there; fp8 caches use twice as many) and the largest batch whose
+// schedule each wave derives by itself.
+constexpr int kBalancedWaves = 1024;
 constexpr int kBalancedMaxSeqs = 1024;
 // Accelerator complex dies of MI355X; consecutive workgroup ids go to
 // consecutive XCDs, each with its own L2.

@@ -101,13 +101,13 @@ def test_null_args_pointer():
 
 def test_split_plan_and_workspace():
     L = pkv.lib()
-    # decode with num_splits == 0 takes the balanced schedule: 2048 waves share
+    # decode with num_splits == 0 takes the balanced schedule: 1024 waves share
     # the KV tiles; the workspace holds a 16-row fp32 partial (+ lse) per
     # (wave + item) slot and the per-request tile prefix
     a = good_args(num_tokens=4, num_seqs=4, num_heads=64, num_kv_heads=8, max_seqlen_k=131072,
                   block_size=256, block_table_stride=512, num_blocks=4096)
-    assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 2048
-    assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == (2048 + 4 * 8) * 16 * (128 + 1) * 4 + (4 + 1) * 4
+    assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 1024
+    assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == (1024 + 4 * 8) * 16 * (128 + 1) * 4 + (4 + 1) * 4
     a.num_splits = 1
     assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 1
     assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == 0
