@@ -680,30 +680,46 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
                                      (__attribute__((address_space(3))) void*)lds_base, 16, OFF, 0);
 }
 
-// K/V tiles of 64 keys live in LDS chunk-major: the 16-byte chunk c (8 bf16
-// elements) of tile row r is at c * kChunkPitch + 16 r, each chunk column
-// padded by 64 bytes. A 16-byte K fragment read (16 consecutive rows of one
-// chunk per 16 lanes) is then contiguous, and a transposed V read (4 rows x 4
-// chunks per 16 lanes) lands the four chunk columns 64 bytes apart, so
-// neither has bank conflicts. Lane l of a 64-lane copy moves tile row l.
+// K/V tiles of 64 keys live in LDS row-major (a key's head_size bf16
+// elements contiguous, no padding), with the 16-byte chunks of each row
+// permuted: chunk c of row r sits at position c ^ lds_swz(r). A 64-lane tile
+// copy then moves whole cache rows (each group of head_size / 8 lanes one
+// row, 16 bytes per lane, which the load unit writes at 16 * lane), and the
+// MFMA operand reads stay free of bank conflicts: a K fragment read (8
+// consecutive rows at one chunk per 8 lanes) and a transposed V read (4 rows
+// x 2 chunks per 16 lanes) each hit distinct 16-byte bank groups. (Copying
+// one 16-byte column of 64 rows per instruction instead, as a chunk-major
+// layout requires, moves the same bytes far more slowly.)
 constexpr int kTileRows = 64;
-constexpr int kChunkPitch = kTileRows * 16 + 64;
+__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
-// POW2: the page size is a power of two (or the layout is flat), so a key's
-// page and offset come from a shift and a mask.
-template <int HD, bool FP8, bool POW2>
+// How a prefill workgroup finds the cache rows of a tile's keys.
+//  kPgAny:  any page size; every key is translated through the block table.
+//  kPgWide: the page size is a power of two of at least 16. The 16 keys a
+//           wave copies in a tile start 16-aligned, so they share one page:
+//           one (wave-uniform) block-table entry per wave and tile.
+//  kPgFlat: no block table; K/V rows are packed like q.
+constexpr int kPgAny = 0, kPgWide = 1, kPgFlat = 2;
+
+template <int HD, bool FP8, int PG>
 __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdParams p) {
     constexpr int NW = kPrefillWaves;           // waves per workgroup
     constexpr int ROWS = prefill_rows(HD);      // query rows per work item
     constexpr int TILE = prefill_tile(HD);      // keys per tile
     constexpr int CPR = HD / 8;                 // 16-byte chunks per row
-    constexpr int CPW = CPR / NW;               // chunk columns each wave copies per tile
+    constexpr int RP = CPR * 16;                // bytes per LDS tile row
+    constexpr int KPI = 64 / CPR;               // keys per 64-lane copy (bf16)
+    constexpr int CPW = TILE / KPI / NW;        // copies per wave per K or V tile (bf16)
+    constexpr int FPR = HD / 16;                // 16-byte fp8 loads per cache row
+    constexpr int FKPI = 64 / FPR;              // keys per 64-lane fp8 load
+    constexpr int FCPW = TILE / FKPI / NW;      // fp8 loads per wave per tile
+    constexpr int NK = FP8 ? FCPW : CPW;        // keys each lane translates per tile
     constexpr int KS = HD / 16;                 // k-steps of S^T = K Q^T (32x32x16)
     constexpr int MB = HD / 32;                 // 32-row blocks of O^T
     constexpr int KB = TILE / 32;               // 32-key blocks per tile
-    constexpr int SLOT = CPR * kChunkPitch;     // bytes of one K or V tile
+    constexpr int SLOT = TILE * RP;             // bytes of one K or V tile
     constexpr int ESZ = FP8 ? 1 : 2;            // bytes per cached element
-    static_assert(TILE == kTileRows && CPW >= 1 && CPR % NW == 0, "");
+    static_assert(TILE == kTileRows && CPW >= 1 && FCPW >= 1 && KPI * RP == 1024, "");
     // K tile j in k_lds<j % 2>, V tile j in v_lds<j % 2>; four separate arrays
     // so that the compiler sees the copies into one slot are independent of
     // the reads of another and does not wait for them
@@ -767,46 +783,85 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         vsc = *p.v_scale;
     }
 
-    // per-lane LDS read offsets; the k-step, key block, output block and key
-    // group parts of each address are immediates
-    // K fragment (kb, ks): tile row kb*32 + (lane & 31), chunk 2 ks + hsel
-    const uint32_t koff = hsel * kChunkPitch + (lane & 31) * 16;
-    // transposed V read (k2, jj, mb): row 16 k2 + 8 jj + 4 hsel + rr,
-    // chunk 4 mb + 2 grp + cc / 2, half cc % 2
-    const uint32_t voff = (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) * kChunkPitch +
-                          (4 * hsel + ((lane & 15) >> 2)) * 16 + (lane & 1) * 8;
-
-    // Tile copies: lane l moves key t0 + l (clamped to the last key, so rows
-    // past the end hold a real, finite key that the mask removes); wave w
-    // moves chunk columns w*CPW .. w*CPW + CPW - 1 of K and of V.
-    const int32_t* bt_row = p.bt ? p.bt + (int64_t)r * p.bt_stride : nullptr;
-    const int64_t rstride = (int64_t)p.Hkv * HD;  // elements per cache row
-    // cache row of this lane's key in the tile starting at t0, in two steps so
-    // the block-table read can be issued an iteration before its use (the
-    // host keeps num_blocks * block_size below 2^31)
-    const int bs_shift = POW2 ? p.bs_shift : -1;
-    auto page_of = [&](int t0) -> int32_t {
-        const int pos = min(t0 + lane, k_end - 1);
-        return bt_row ? bt_row[POW2 ? pos >> bs_shift : pos / p.bs] : 0;
-    };
-    auto row_from = [&](int t0, int32_t page) -> int32_t {
-        const int pos = min(t0 + lane, k_end - 1);
-        return bt_row ? page * p.bs + (POW2 ? pos & (p.bs - 1) : pos % p.bs) : q0 + pos;
-    };
-    using raw_t = u32x2;  // fp8: 8 cached bytes per chunk, widened in registers
-    raw_t st_k[CPW], st_v[CPW];
-    auto issue = [&](const void* cache, int32_t row, uint8_t* slot, raw_t* st) {
-        const uint8_t* src = (const uint8_t*)cache + (((int64_t)row * p.Hkv + kh) * HD + w * CPW * 8) * ESZ;
+    // Per-lane LDS read offsets. The permutation only touches the low three
+    // bits of a chunk index and depends on r & 7, so the higher chunk bits,
+    // the key block and the row group of each read are immediates.
+    // K fragment (kb, ks): row kb*32 + (lane & 31), chunk 2 ks + hsel; its
+    // position is (2 ks & ~7) + ((2 (ks & 3) + hsel) ^ swz(row)).
+    uint32_t koffs[4];
+    {
+        const int rk = lane & 31;
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            if constexpr (FP8) st[c] = *(const raw_t*)(src + c * 8);
-            else copy16_to_lds<0>(src + c * 16, slot + (w * CPW + c) * kChunkPitch);
+        for (int j = 0; j < 4; ++j) koffs[j] = rk * RP + (((2 * j + hsel) ^ lds_swz(rk)) & (CPR - 1)) * 16;
+    }
+    // transposed V read (k2, hi, mb): row 16 k2 + 8 hi + 4 hsel + (lane & 15) / 4,
+    // chunk 4 mb + cp with cp = 2 ((lane >> 4) & 1) + (lane & 3) / 2, half
+    // lane & 1; position (4 mb & ~7) + ((4 (mb & 1) + cp) ^ swz(row)).
+    uint32_t voffs[2];
+    {
+        const int rv = 4 * hsel + ((lane & 15) >> 2);
+        const int cp = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            voffs[j] = rv * RP + (((4 * j + cp) ^ lds_swz(rv)) & (CPR - 1)) * 16 + (lane & 1) * 8;
+    }
+
+    // Tile copies. bf16: copy jj of wave w moves keys (w CPW + jj) KPI ..
+    // + KPI - 1, lane l the 16-byte chunk at position l % CPR of key
+    // (w CPW + jj) KPI + l / CPR. fp8: load jj of wave w reads 16 cached
+    // bytes (chunks 2q and 2q + 1, q = l % FPR) of key (w FCPW + jj) FKPI +
+    // l / FPR, widened to bf16 in registers and stored. Keys are clamped to
+    // the last key of the range, so rows past the end hold a real, finite key
+    // that the mask removes.
+    const int32_t* bt_row = p.bt ? p.bt + (int64_t)r * p.bt_stride : nullptr;
+    constexpr int NP = PG == kPgAny ? NK : 1;   // block-table entries a lane holds per tile
+    auto key_of = [&](int jj) -> int {
+        if constexpr (FP8) return (w * FCPW + jj) * FKPI + lane / FPR;
+        else return (w * CPW + jj) * KPI + lane / CPR;
+    };
+    // The cache rows of this lane's keys in the tile starting at t0 come in
+    // two steps, so that the block-table reads can be issued an iteration
+    // before their use: page_of reads the entries, row_of forms a row (the
+    // host keeps num_blocks * block_size below 2^31).
+    auto page_of = [&](int t0, int32_t (&pg)[NP]) {
+        if constexpr (PG == kPgAny) {
+#pragma unroll
+            for (int jj = 0; jj < NK; ++jj) pg[jj] = bt_row[min(t0 + key_of(jj), k_end - 1) / p.bs];
+        } else if constexpr (PG == kPgWide) {
+            pg[0] = bt_row[min(t0 + 16 * w, k_end - 1) >> p.bs_shift];
+        } else {
+            pg[0] = 0;
         }
     };
-    // fp8: widen the staged chunks and store them
-    auto land = [&](uint8_t* slot, const raw_t* st) {
+    auto row_of = [&](int t0, const int32_t (&pg)[NP], int jj) -> int32_t {
+        const int pos = min(t0 + key_of(jj), k_end - 1);
+        if constexpr (PG == kPgAny) return pg[jj] * p.bs + pos % p.bs;
+        else if constexpr (PG == kPgWide) return pg[0] * p.bs + (pos & (p.bs - 1));
+        else return q0 + pos;
+    };
+    u32x4 st_k[NK], st_v[NK];  // fp8 staging
+    auto issue = [&](const void* cache, int t0, const int32_t (&pg)[NP], uint8_t* slot, u32x4 (&st)[NK]) {
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) *(u32x4*)(slot + (w * CPW + c) * kChunkPitch + lane * 16) = fp8x8_to_bf16x8(st[c]);
+        for (int jj = 0; jj < NK; ++jj) {
+            // first element of the key's head row
+            const int64_t rowe = ((int64_t)row_of(t0, pg, jj) * p.Hkv + kh) * HD;
+            if constexpr (FP8) {
+                st[jj] = *(const u32x4*)((const uint8_t*)cache + rowe + (lane % FPR) * 16);
+            } else {
+                const int chunk = (lane % CPR) ^ (lds_swz(key_of(jj)) & (CPR - 1));
+                copy16_to_lds<0>((const uint16_t*)cache + rowe + chunk * 8, slot + (w * CPW + jj) * 1024);
+            }
+        }
+    };
+    // fp8: widen the staged bytes and store them at their permuted positions
+    auto land = [&](uint8_t* slot, const u32x4 (&st)[NK]) {
+#pragma unroll
+        for (int jj = 0; jj < NK; ++jj) {
+            const int key = key_of(jj), q = lane % FPR, sw = lds_swz(key) & (CPR - 1);
+            uint8_t* row = slot + key * RP;
+            *(u32x4*)(row + ((2 * q) ^ sw) * 16) = fp8x8_to_bf16x8(u32x2{st[jj].x, st[jj].y});
+            *(u32x4*)(row + ((2 * q + 1) ^ sw) * 16) = fp8x8_to_bf16x8(u32x2{st[jj].z, st[jj].w});
+        }
     };
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -824,7 +879,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
             for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                sacc[kb] = mfma32x32x16(*(const u32x4*)(kslot + koff + 2 * ks * kChunkPitch + kb * 512), qf[ks], sacc[kb]);
+                sacc[kb] = mfma32x32x16(
+                    *(const u32x4*)(kslot + koffs[ks & 3] + ((2 * ks) & ~7) * 16 + kb * 32 * RP), qf[ks], sacc[kb]);
         }
     };
     // causal / length mask of a tile that reaches past wave_min
@@ -885,9 +941,9 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int k2 = 0; k2 < 2 * KB; ++k2) {
-                const uint8_t* vp = vslot + voff + 4 * mb * kChunkPitch + 16 * k2 * 16;
+                const uint8_t* vp = vslot + voffs[mb & 1] + ((4 * mb) & ~7) * 16 + 16 * k2 * RP;
                 const u32x2 lo = lds_read_tr16(vp);
-                const u32x2 hi = lds_read_tr16(vp + 8 * 16);
+                const u32x2 hi = lds_read_tr16(vp + 8 * RP);
                 oacc[mb] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pf[k2], oacc[mb]);
             }
     };
@@ -901,22 +957,23 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     const int n_tiles = (k_end - k_begin + TILE - 1) / TILE;
     f32x16 s_a[KB], s_b[KB];
     float mx;
-    int32_t row_v;  // cache row of this lane's key in tile i+1 (for V(i+1))
-    int32_t pg_k;   // block-table entry of this lane's key in tile i+2 (for K(i+2))
+    int32_t pg_v[NP];  // block-table entries of this lane's keys in tile i+1 (for V(i+1))
+    int32_t pg_k[NP];  // block-table entries of this lane's keys in tile i+2 (for K(i+2))
     {
-        const int32_t row0 = row_from(k_begin, page_of(k_begin));
-        issue(p.k_cache, row0, k_lds0, st_k);
-        issue(p.v_cache, row0, v_lds0, st_v);
+        int32_t pg0[NP];
+        page_of(k_begin, pg0);
+        issue(p.k_cache, k_begin, pg0, k_lds0, st_k);
+        issue(p.v_cache, k_begin, pg0, v_lds0, st_v);
         if constexpr (FP8) {
             land(k_lds0, st_k);  // (waits for its loads)
             land(v_lds0, st_v);
         }
-        row_v = row_from(k_begin + TILE, page_of(k_begin + TILE));
+        page_of(k_begin + TILE, pg_v);
         if (n_tiles > 1) {
-            issue(p.k_cache, row_v, k_lds1, st_k);
+            issue(p.k_cache, k_begin + TILE, pg_v, k_lds1, st_k);
             if constexpr (FP8) land(k_lds1, st_k);
         }
-        pg_k = page_of(k_begin + 2 * TILE);
+        page_of(k_begin + 2 * TILE, pg_k);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         qk(k_lds0, s_a);
@@ -933,14 +990,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         uint8_t* const v_next = P ? v_lds0 : v_lds1;   // receives V(i+1)
         const int t0 = k_begin + i * TILE;
         const bool load_k = i + 2 < n_tiles;
-        int32_t row_k = 0;
+        int32_t pg_kk[NP];  // entries of tile i+2: V(i+2) is issued from them next iteration
+#pragma unroll
+        for (int jj = 0; jj < NP; ++jj) pg_kk[jj] = pg_k[jj];
         if constexpr (!LAST) {
-            if (load_k) {
-                row_k = row_from(t0 + 2 * TILE, pg_k);
-                issue(p.k_cache, row_k, k_here, st_k);
-            }
-            issue(p.v_cache, row_v, v_next, st_v);
-            if (i + 3 < n_tiles) pg_k = page_of(t0 + 3 * TILE);
+            if (load_k) issue(p.k_cache, t0 + 2 * TILE, pg_k, k_here, st_k);
+            issue(p.v_cache, t0 + TILE, pg_v, v_next, st_v);
+            if (i + 3 < n_tiles) page_of(t0 + 3 * TILE, pg_k);
         }
         rescale(mx);
         u32x4 pf[2 * KB];
@@ -954,7 +1010,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
                 if (load_k) land(k_here, st_k);
                 land(v_next, st_v);
             }
-            row_v = row_k;
+#pragma unroll
+            for (int jj = 0; jj < NP; ++jj) pg_v[jj] = pg_kk[jj];
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
@@ -1351,13 +1408,15 @@ static hipError_t prefill_hd(const FwdParams& p, KvType kv, hipStream_t s) {
     const int64_t streams_per_xcd = ((int64_t)p.B * p.Hkv + kXcds - 1) / kXcds;
     dim3 grid((unsigned)(streams_per_xcd * kXcds * p.n_qtiles), p.num_splits);
     const dim3 block(64 * kPrefillWaves);
-    const bool pow2 = !p.bt || p.bs_shift >= 0;
+    const int pg = !p.bt ? kPgFlat : (p.bs_shift >= 4 ? kPgWide : kPgAny);
     if (kv == KvType::FP8) {
-        if (pow2) hipLaunchKernelGGL((prefill_kernel<HD, true, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((prefill_kernel<HD, true, false>), grid, block, 0, s, p);
+        if (pg == kPgFlat) hipLaunchKernelGGL((prefill_kernel<HD, true, kPgFlat>), grid, block, 0, s, p);
+        else if (pg == kPgWide) hipLaunchKernelGGL((prefill_kernel<HD, true, kPgWide>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((prefill_kernel<HD, true, kPgAny>), grid, block, 0, s, p);
     } else {
-        if (pow2) hipLaunchKernelGGL((prefill_kernel<HD, false, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((prefill_kernel<HD, false, false>), grid, block, 0, s, p);
+        if (pg == kPgFlat) hipLaunchKernelGGL((prefill_kernel<HD, false, kPgFlat>), grid, block, 0, s, p);
+        else if (pg == kPgWide) hipLaunchKernelGGL((prefill_kernel<HD, false, kPgWide>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((prefill_kernel<HD, false, kPgAny>), grid, block, 0, s, p);
     }
     return hipGetLastError();
 }

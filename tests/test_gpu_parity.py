@@ -140,6 +140,8 @@ PREFILL_CASES = [
     ([33, 20], [5, 100], 12, 3, 128, 5),     # g = 4 with a page size of 5
     ([45, 17], [0, 33], 6, 2, 128, 16),      # g = 3: rows per workgroup not a multiple of g
     ([50, 0, 60], [7, 9, 0], 8, 8, 128, 1),  # page size 1 and an empty request
+    ([70, 130], [500, 33], 16, 4, 128, 32),  # pages of 32 and 256 keys
+    ([66, 3], [700, 260], 8, 2, 128, 256),
 ]
 
 
@@ -175,9 +177,10 @@ def test_fp8_cache_decode_parity(bs):
     run_and_check(prob, 0, what=f"fp8 decode bs={bs}")
 
 
-def test_fp8_cache_prefill_parity():
-    prob = workloads.make_problem(501, [70, 33], [100, 0], H=8, Hkv=2, hd=128, bs=16, cache_dtype="fp8")
-    run_and_check(prob, 1, what="fp8 prefill")
+@pytest.mark.parametrize("hd,bs", [(128, 16), (128, 5), (64, 8), (256, 32)])
+def test_fp8_cache_prefill_parity(hd, bs):
+    prob = workloads.make_problem(501, [70, 33], [100, 0], H=8, Hkv=2, hd=hd, bs=bs, cache_dtype="fp8")
+    run_and_check(prob, 1, what=f"fp8 prefill hd={hd} bs={bs}")
 
 
 def test_flat_bf16_prefill_parity():
