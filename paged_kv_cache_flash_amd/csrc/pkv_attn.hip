@@ -681,17 +681,55 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
 }
 
 // K/V tiles of 64 keys live in LDS row-major (a key's head_size bf16
-// elements contiguous, no padding), with the 16-byte chunks of each row
-// permuted: chunk c of row r sits at position c ^ lds_swz(r). A 64-lane tile
-// copy then moves whole cache rows (each group of head_size / 8 lanes one
-// row, 16 bytes per lane, which the load unit writes at 16 * lane), and the
-// MFMA operand reads stay free of bank conflicts: a K fragment read (8
-// consecutive rows at one chunk per 8 lanes) and a transposed V read (4 rows
-// x 2 chunks per 16 lanes) each hit distinct 16-byte bank groups. (Copying
-// one 16-byte column of 64 rows per instruction instead, as a chunk-major
-// layout requires, moves the same bytes far more slowly.)
+// elements contiguous). A 64-lane tile copy moves whole cache rows: each group
+// of head_size / 8 lanes reads one row, 16 bytes per lane, and the load unit
+// writes them at 16 * lane, so one copy fills 1 KB of consecutive rows (a
+// "copy group"). The layout then adds PAD bytes after each copy group and
+// permutes the 16-byte chunks of row r: chunk c sits at position c ^ sw(r).
+// PAD and sw are chosen per head size so that, with the 64 four-byte LDS banks
+// of gfx950 (16 lanes per clock for 16-byte reads, 32 for 8-byte reads), the
+// K fragment reads and the transposed V reads of the MFMA loop hit every bank
+// at most once. (Copying one 16-byte column of 64 rows per instruction
+// instead, as a chunk-major layout requires, moves the same bytes far more
+// slowly.)
+template <int HD>
+struct PfLayout;
+template <>
+struct PfLayout<64> {
+    static constexpr int PAD = 16, A0 = 0, A1 = 4, A2 = 2, A3 = 0;
+};
+template <>
+struct PfLayout<128> {
+    static constexpr int PAD = 16, A0 = 4, A1 = 8, A2 = 0, A3 = 0;
+};
+template <>
+struct PfLayout<256> {
+    static constexpr int PAD = 64, A0 = 8, A1 = 0, A2 = 1, A3 = 2;
+};
+template <int HD>
+struct PfTile {
+    using L = PfLayout<HD>;
+    static constexpr int CPR = HD / 8;                 // 16-byte chunks per row
+    static constexpr int RP = CPR * 16;                // bytes per row
+    static constexpr int KPI = 64 / CPR;               // rows per copy group
+    static constexpr int GP = 1024 + L::PAD;           // bytes per copy group
+    static constexpr int SWMASK = L::A0 | L::A1 | L::A2 | L::A3;
+    static_assert(SWMASK < CPR && KPI * RP == 1024, "");
+    static __device__ __forceinline__ int sw(int r) {
+        return (L::A0 * (r & 1)) ^ (L::A1 * ((r >> 1) & 1)) ^ (L::A2 * ((r >> 2) & 1)) ^ (L::A3 * ((r >> 3) & 1));
+    }
+    // byte offset of row r's first position
+    static __device__ __forceinline__ int row_base(int r) { return (r / KPI) * GP + (r % KPI) * RP; }
+};
+// Index of the bits of x selected by mask, packed (a compile-time pext).
+constexpr int pext(int x, int mask) {
+    int r = 0, k = 0;
+    for (int b = 0; b < 16; ++b)
+        if (mask & (1 << b)) r |= ((x >> b) & 1) << k++;
+    return r;
+}
+constexpr int popcount(int x) { return x ? (x & 1) + popcount(x >> 1) : 0; }
 constexpr int kTileRows = 64;
-__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 // How a prefill workgroup finds the cache rows of a tile's keys.
 //  kPgAny:  any page size; every key is translated through the block table.
@@ -707,7 +745,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     constexpr int ROWS = prefill_rows(HD);      // query rows per work item
     constexpr int TILE = prefill_tile(HD);      // keys per tile
     constexpr int CPR = HD / 8;                 // 16-byte chunks per row
-    constexpr int RP = CPR * 16;                // bytes per LDS tile row
+    using PT = PfTile<HD>;                      // LDS tile layout
     constexpr int KPI = 64 / CPR;               // keys per 64-lane copy (bf16)
     constexpr int CPW = TILE / KPI / NW;        // copies per wave per K or V tile (bf16)
     constexpr int FPR = HD / 16;                // 16-byte fp8 loads per cache row
@@ -717,9 +755,9 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     constexpr int KS = HD / 16;                 // k-steps of S^T = K Q^T (32x32x16)
     constexpr int MB = HD / 32;                 // 32-row blocks of O^T
     constexpr int KB = TILE / 32;               // 32-key blocks per tile
-    constexpr int SLOT = TILE * RP;             // bytes of one K or V tile
+    constexpr int SLOT = TILE / PT::KPI * PT::GP;  // bytes of one K or V tile
     constexpr int ESZ = FP8 ? 1 : 2;            // bytes per cached element
-    static_assert(TILE == kTileRows && CPW >= 1 && FCPW >= 1 && KPI * RP == 1024, "");
+    static_assert(TILE == kTileRows && CPW >= 1 && FCPW >= 1 && KPI == PT::KPI, "");
     // K tile j in k_lds<j % 2>, V tile j in v_lds<j % 2>; four separate arrays
     // so that the compiler sees the copies into one slot are independent of
     // the reads of another and does not wait for them
@@ -783,27 +821,48 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         vsc = *p.v_scale;
     }
 
-    // Per-lane LDS read offsets. The permutation only touches the low three
-    // bits of a chunk index and depends on r & 7, so the higher chunk bits,
-    // the key block and the row group of each read are immediates.
-    // K fragment (kb, ks): row kb*32 + (lane & 31), chunk 2 ks + hsel; its
-    // position is (2 ks & ~7) + ((2 (ks & 3) + hsel) ^ swz(row)).
-    uint32_t koffs[4];
+    // Per-lane LDS read offsets. The chunk permutation only touches the bits
+    // in SWMASK and depends on row bits 0..3, so the other chunk bits, the
+    // key block and the row group of each read are immediates; one offset
+    // per pattern of the masked chunk bits.
+    // K fragment (kb, ks): row kb*32 + (lane & 31), chunk 2 ks + hsel.
+    constexpr int KPAT = 1 << popcount((2 * (KS - 1)) & PT::SWMASK & ~1);
+    uint32_t koffs[KPAT];
     {
         const int rk = lane & 31;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) koffs[j] = rk * RP + (((2 * j + hsel) ^ lds_swz(rk)) & (CPR - 1)) * 16;
+        for (int j = 0; j < KPAT; ++j) {
+            // the masked chunk bits of pattern j (bit 0 is hsel's, never 2 ks's)
+            int cm = 0, k = 0;
+#pragma unroll
+            for (int b = 1; b < 16; ++b)
+                if (PT::SWMASK & ~1 & (1 << b)) cm |= ((j >> k++) & 1) << b;
+            const int c_lane = cm | hsel;  // chunk bits that vary with the lane or the pattern
+            koffs[j] = PT::row_base(rk) + ((c_lane & PT::SWMASK) ^ PT::sw(rk)) * 16 + (c_lane & ~PT::SWMASK) * 16;
+        }
     }
     // transposed V read (k2, hi, mb): row 16 k2 + 8 hi + 4 hsel + (lane & 15) / 4,
     // chunk 4 mb + cp with cp = 2 ((lane >> 4) & 1) + (lane & 3) / 2, half
-    // lane & 1; position (4 mb & ~7) + ((4 (mb & 1) + cp) ^ swz(row)).
-    uint32_t voffs[2];
+    // lane & 1. Row bit 3 (hi) enters the permutation only through A3.
+    constexpr int VPAT = 1 << popcount((4 * (MB - 1)) & PT::SWMASK & ~3);
+    constexpr int VHI = PfLayout<HD>::A3 ? 2 : 1;
+    uint32_t voffs[VHI][VPAT];
     {
-        const int rv = 4 * hsel + ((lane & 15) >> 2);
         const int cp = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            voffs[j] = rv * RP + (((4 * j + cp) ^ lds_swz(rv)) & (CPR - 1)) * 16 + (lane & 1) * 8;
+        for (int h = 0; h < VHI; ++h) {
+            const int rv = 8 * h + 4 * hsel + ((lane & 15) >> 2);
+#pragma unroll
+            for (int j = 0; j < VPAT; ++j) {
+                int cm = 0, k = 0;
+#pragma unroll
+                for (int b = 2; b < 16; ++b)
+                    if (PT::SWMASK & ~3 & (1 << b)) cm |= ((j >> k++) & 1) << b;
+                const int c_lane = cm | cp;
+                voffs[h][j] = PT::row_base(rv) - (VHI == 2 && h ? PT::row_base(8) : 0) +
+                              ((c_lane & PT::SWMASK) ^ PT::sw(rv)) * 16 + (c_lane & ~PT::SWMASK) * 16 + (lane & 1) * 8;
+            }
+        }
     }
 
     // Tile copies. bf16: copy jj of wave w moves keys (w CPW + jj) KPI ..
@@ -848,8 +907,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
             if constexpr (FP8) {
                 st[jj] = *(const u32x4*)((const uint8_t*)cache + rowe + (lane % FPR) * 16);
             } else {
-                const int chunk = (lane % CPR) ^ (lds_swz(key_of(jj)) & (CPR - 1));
-                copy16_to_lds<0>((const uint16_t*)cache + rowe + chunk * 8, slot + (w * CPW + jj) * 1024);
+                const int chunk = (lane % CPR) ^ PT::sw(key_of(jj));
+                copy16_to_lds<0>((const uint16_t*)cache + rowe + chunk * 8, slot + (w * CPW + jj) * PT::GP);
             }
         }
     };
@@ -857,8 +916,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     auto land = [&](uint8_t* slot, const u32x4 (&st)[NK]) {
 #pragma unroll
         for (int jj = 0; jj < NK; ++jj) {
-            const int key = key_of(jj), q = lane % FPR, sw = lds_swz(key) & (CPR - 1);
-            uint8_t* row = slot + key * RP;
+            const int key = key_of(jj), q = lane % FPR, sw = PT::sw(key);
+            uint8_t* row = slot + PT::row_base(key);
             *(u32x4*)(row + ((2 * q) ^ sw) * 16) = fp8x8_to_bf16x8(u32x2{st[jj].x, st[jj].y});
             *(u32x4*)(row + ((2 * q + 1) ^ sw) * 16) = fp8x8_to_bf16x8(u32x2{st[jj].z, st[jj].w});
         }
@@ -880,7 +939,9 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 sacc[kb] = mfma32x32x16(
-                    *(const u32x4*)(kslot + koffs[ks & 3] + ((2 * ks) & ~7) * 16 + kb * 32 * RP), qf[ks], sacc[kb]);
+                    *(const u32x4*)(kslot + koffs[pext(2 * ks, PT::SWMASK & ~1)] + ((2 * ks) & ~PT::SWMASK) * 16 +
+                                    kb * PT::row_base(32)),
+                    qf[ks], sacc[kb]);
         }
     };
     // causal / length mask of a tile that reaches past wave_min
@@ -941,9 +1002,10 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int k2 = 0; k2 < 2 * KB; ++k2) {
-                const uint8_t* vp = vslot + voffs[mb & 1] + ((4 * mb) & ~7) * 16 + 16 * k2 * RP;
-                const u32x2 lo = lds_read_tr16(vp);
-                const u32x2 hi = lds_read_tr16(vp + 8 * RP);
+                const int vj = pext(4 * mb, PT::SWMASK & ~3);
+                const uint8_t* vp = vslot + ((4 * mb) & ~PT::SWMASK) * 16 + k2 * PT::row_base(16);
+                const u32x2 lo = lds_read_tr16(vp + voffs[0][vj]);
+                const u32x2 hi = lds_read_tr16(vp + voffs[VHI - 1][vj] + PT::row_base(8));
                 oacc[mb] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pf[k2], oacc[mb]);
             }
     };
