@@ -163,7 +163,12 @@ int or_cache_write(const void* key, const void* value, int src_dtype,
                    float k_scale, float v_scale) {
     if (!(src_dtype == OR_F32 || src_dtype == OR_BF16)) return -1;
     if (cache_dtype == OR_F32 && src_dtype != OR_F32) return -1;
+    if (!(cache_dtype == src_dtype || cache_dtype == OR_BF16 || cache_dtype == OR_E4M3FN)) return -1;
+    if (cache_dtype == OR_E4M3FN) e4m3_table_init();
     int64_t row = (int64_t)Hkv * hd;
+    /* Tokens are independent (their slots are distinct), so they may be
+     * written in any order; each element is encoded exactly as below. */
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         int64_t slot = slot_mapping[t];
         if (slot < 0) continue;
@@ -184,8 +189,6 @@ int or_cache_write(const void* key, const void* value, int src_dtype,
                     float x = (float)load_elem(src, src_dtype, si); /* exact */
                     volatile float y = x / sc;                      /* binary32 division, round to nearest */
                     ((uint8_t*)dst)[di] = or_encode_e4m3fn(y);
-                } else {
-                    return -1;
                 }
             }
         }

@@ -77,10 +77,21 @@ class GpuProblem:
                                   v_scale=self.v_scale, num_splits=num_splits, return_lse=True)
 
 
-def oracle_cache(prob):
+def oracle_cache(prob, requests=None):
+    """The oracle's own cache write of every cached token, or only of the
+    tokens of ``requests`` (the rest of the cache keeps its NaN poison, which
+    attention over those requests never reads)."""
     kc, vc = prob.empty_cache()
-    return oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc, vc, prob.kv_slots, prob.bs,
+    rows = np.arange(len(prob.kv_src_k))
+    if requests is not None:
+        rows = np.unique(np.concatenate([prob.pos_rows[r] for r in requests]))
+    return oracle.cache_write(prob.kv_src_k[rows], prob.kv_src_v[rows], kc, vc, prob.kv_slots[rows], prob.bs,
                               k_scale=prob.k_scale, v_scale=prob.v_scale)
+
+
+def requests_of(prob, rows):
+    """Requests owning packed query rows."""
+    return np.unique(np.searchsorted(prob.query_start_loc, np.asarray(rows), side="right") - 1)
 
 
 def oracle_attention(prob, rows=None, causal=None, caches=None):

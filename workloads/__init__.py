@@ -11,7 +11,9 @@ Llama-3-8B-like GQA layout of 32 query / 8 kv heads, head size 128):
   * lengths are drawn first, integers uniform inclusive, from
     ``numpy.random.default_rng(seed)`` (PCG64);
   * then Q, K, V ~ N(0, 1) in float32, rounded to nearest-even bfloat16 when
-    the storage type is bf16;
+    the storage type is bf16 (arrays of more than 4M elements are drawn in
+    4M-element chunks from child generators spawned from one seed taken from
+    the same generator, so large workloads generate on several threads);
   * physical pages are a random permutation drawn from a second generator
     ``default_rng(seed + 100)``; each request takes its pages in order from it;
     one extra page is the poison page (NaN in every element) and every unused
@@ -49,13 +51,37 @@ def storage_to_f32(a: np.ndarray) -> np.ndarray:
     raise TypeError(a.dtype)
 
 
+# Arrays above this many elements are drawn in chunks of this size, each
+# chunk from its own child generator, on several threads.
+_CHUNK = 1 << 22
+
+
 def _draw(rng, shape, dtype):
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if dtype == "bf16":
-        return to_bf16_bits(x)
-    if dtype == "f32":
-        return x
-    raise ValueError(dtype)
+    """N(0, 1) in float32 (rounded to bf16 if asked). Small arrays come from
+    ``rng`` itself; a larger one is split into chunks of _CHUNK elements, and
+    chunk i is drawn from default_rng(child i) where the children are
+    SeedSequence(s).spawn(n_chunks) for one integer s drawn from ``rng``: the
+    values depend on the seed only, not on the thread count."""
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(dtype)
+    n = int(np.prod(shape))
+    if n <= _CHUNK:
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        return to_bf16_bits(x) if dtype == "bf16" else x
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    n_chunks = -(-n // _CHUNK)
+    children = np.random.SeedSequence(int(rng.integers(2 ** 63))).spawn(n_chunks)
+    out = np.empty(n, np.uint16 if dtype == "bf16" else np.float32)
+
+    def fill(i):
+        a, b = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        x = np.random.default_rng(children[i]).standard_normal(b - a, dtype=np.float32)
+        out[a:b] = to_bf16_bits(x) if dtype == "bf16" else x
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(n_chunks)))
+    return out.reshape(shape)
 
 
 @dataclass
@@ -177,6 +203,21 @@ def make_problem(seed: int, q_lens, ctx_lens, *, H: int, Hkv: int, hd: int, bs: 
         prob.v_scale = float(np.float32(np.abs(storage_to_f32(vsrc)).max() / np.float32(448.0)))
     if not paged:
         return prob
+    return _page(prob, bs, seed, extra_blocks, table_slack)
+
+
+def with_page_size(prob: Problem, bs: int, seed: int, extra_blocks: int = 0, table_slack: int = 0) -> Problem:
+    """The same logical batch (same q, K, V rows, lengths and scales) laid out
+    in pages of ``bs`` tokens, with a fresh random page assignment."""
+    from dataclasses import replace
+    return _page(replace(prob, bs=bs), bs, seed, extra_blocks, table_slack)
+
+
+def _page(prob: Problem, bs: int, seed: int, extra_blocks: int, table_slack: int) -> Problem:
+    """Random physical page assignment, block table and slot mapping."""
+    B, seq_lens, shared_prefix, pos_rows = prob.B, prob.seq_lens, prob.shared_prefix, prob.pos_rows
+    n_rows = len(prob.kv_src_k)
+    assert shared_prefix % bs == 0
     # page allocation: a random permutation of physical pages
     pre_pages = shared_prefix // bs
     own_pages = [-(-(int(seq_lens[r]) - shared_prefix) // bs) for r in range(B)]
