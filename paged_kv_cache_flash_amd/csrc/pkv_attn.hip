@@ -585,32 +585,48 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
 #pragma unroll
     for (int i = 0; i < MB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // The end of an item segment: the final output when the segment is the
-    // whole item, else a partial state in slot (wave + item).
-    auto finish = [&](const DecodeCursor& c) {
+    // The end of an item segment, in two steps. close(): normalise the
+    // running output in place (oacc *= 1/l) and form its lse. write(): store
+    // it, as the final output when the segment is the whole item, else as a
+    // partial state in slot (wave + item); then reset the running state.
+    // write() runs at the top of the next iteration, before that iteration's
+    // loads: its stores then retire behind nothing, and the wait for the
+    // next tile's loads covers them at no cost. (Issued after the loads, the
+    // stores would have to be waited for on their own, a stall at every item
+    // boundary a wave crosses.)
+    float w_lse = 0.f;
+    bool w_whole = false;
+    DecodeCursor wc = c0;
+    auto close = [&](const DecodeCursor& c) {
         float l = l_run;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        if (row < c.q_len * p.g) {
-            const float inv = l > 0.f ? vsc / l : 0.f;
-            const float mu = m_run == -INFINITY ? 0.f : m_run;
-            const float lse = l > 0.f ? (mu + fast_log2(l)) * kLn2 : -INFINITY;
-            if (seg_t0 == 0 && c.t == c.n - 1) {
-                const int64_t tok = c.q0 + row / p.g;
-                const int head = c.kh * p.g + row % p.g;
+        const float inv = l > 0.f ? vsc / l : 0.f;
+        const float mu = m_run == -INFINITY ? 0.f : m_run;
+        w_lse = l > 0.f ? (mu + fast_log2(l)) * kLn2 : -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb] *= inv;
+        w_whole = seg_t0 == 0 && c.t == c.n - 1;
+        wc = c;
+    };
+    auto write = [&]() {
+        if (row < wc.q_len * p.g) {
+            if (w_whole) {
+                const int64_t tok = wc.q0 + row / p.g;
+                const int head = wc.kh * p.g + row % p.g;
                 uint16_t* op = (uint16_t*)p.out + (tok * p.H + head) * HD + G * 4;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
-                    float v4[4] = {oacc[mb][0] * inv, oacc[mb][1] * inv, oacc[mb][2] * inv, oacc[mb][3] * inv};
+                    float v4[4] = {oacc[mb][0], oacc[mb][1], oacc[mb][2], oacc[mb][3]};
                     store_bf16<4>(op + mb * 16, v4);
                 }
-                if (p.lse && G == 0) p.lse[(int64_t)head * p.T + tok] = lse;
+                if (p.lse && G == 0) p.lse[(int64_t)head * p.T + tok] = w_lse;
             } else {
-                const int64_t slot = gw + (int64_t)c.r * p.Hkv + c.kh;
+                const int64_t slot = gw + (int64_t)wc.r * p.Hkv + wc.kh;
                 float* op = p.part_o + (slot * 16 + row) * HD + G * 4;
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) *(f32x4*)(op + mb * 16) = oacc[mb] * inv;
-                if (G == 0) p.part_lse[slot * 16 + row] = lse;
+                for (int mb = 0; mb < MB; ++mb) *(f32x4*)(op + mb * 16) = oacc[mb];
+                if (G == 0) p.part_lse[slot * 16 + row] = w_lse;
             }
         }
         m_run = -INFINITY;
@@ -620,12 +636,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     };
 
     // One software pipeline over the wave's whole tile range, across item
-    // boundaries: iteration i requests the block-table entries of tile i+2,
-    // issues the K/V loads of tile i+1 (and, when tile i+1 opens another
-    // item, that item's query fragment), computes tile i from LDS, closes
-    // tile i's item segment if it ends there, and moves tile i+1 into LDS.
-    // A new item therefore costs no pipeline restart. Past the wave's range
-    // the last tile is re-read (cached) and never computed.
+    // boundaries: iteration i writes out the segment tile i-1 closed (if
+    // any), requests the block-table entries of tile i+2, issues the K/V
+    // loads of tile i+1 (and, when tile i+1 opens another item, that item's
+    // query fragment), computes tile i from LDS, closes tile i's item segment
+    // if it ends there, and moves tile i+1 into LDS. A new item therefore
+    // costs no pipeline restart. Past the wave's range the last tile is
+    // re-read (cached) and never computed.
     u32x4 kr[NL], vr[NL];
     int pg[NL], rows[NL];
     page_for(c0, pg);
@@ -634,14 +651,20 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     DT::load(p, lane, rows, c0.kh, kr, vr);
     row_from(c1, pg, rows);
     DT::store(stage, lane, kr, vr);
+    bool pending = false;
     while (true) {
+        if (pending) write();
+        pending = false;
         page_for(c2, pg);
         DT::load(p, lane, rows, c1.kh, kr, vr);
         const bool c1_new = c1.valid && c1.t == 0;
         if (c1_new) load_decode_q<HD>(p, lane, c1.q0, c1.q_len * p.g, c1.kh, qn);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
         DT::compute(stage, lane, c0.t * TILE, limit, sl2, qf, m_run, l_run, oacc);
-        if (!c1.valid || c1_new) finish(c0);
+        if (!c1.valid || c1_new) {
+            close(c0);
+            pending = true;
+        }
         if (!c1.valid) break;
         row_from(c2, pg, rows);
         c0 = c1;
@@ -655,12 +678,12 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
         }
         DT::store(stage, lane, kr, vr);
         // Nothing may be left in flight here: the next iteration's loads are
-        // then the only ones its waits count (the output stores of a finished
-        // segment and the query loads would otherwise make the compiler wait
-        // on every tile load it issues).
+        // then the only ones its waits count (the query loads would otherwise
+        // make the compiler wait on every tile load it issues).
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __builtin_amdgcn_sched_barrier(0);
     }
+    write();  // the wave's last segment
 }
 
 // ----------------------------------------------------------------- prefill
