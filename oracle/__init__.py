@@ -26,6 +26,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pkv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A prebuilt oracle library to load instead (the mutation tests point this at
+# copies of the oracle with a planted mistake); it is used as is, never built.
+_LIB_OVERRIDE = os.environ.get("PKV_ORACLE_LIB")
 
 F32, BF16, E4M3FN = 0, 1, 2
 
@@ -47,8 +50,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            L = ctypes.CDLL(_LIB_PATH)
         vp, i32, i64, dbl, flt = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float
         L.or_decode_e4m3fn.restype = dbl
         L.or_decode_e4m3fn.argtypes = [ctypes.c_uint8]
