@@ -69,6 +69,8 @@ def lib():
         common = [vp, i32, vp, vp, i32, dbl, dbl, vp, vp, vp, i64, i32, i32, i32, i32, i32, dbl, i32]
         L.or_attention.restype = i32
         L.or_attention.argtypes = common + [vp, i64, vp, vp, i32]
+        L.or_attention_ex.restype = i32
+        L.or_attention_ex.argtypes = common + [i64, dbl, vp, vp, i64, vp, vp, i32]
         for nm in ("or_attention_online", "or_attention_online_normalised"):
             getattr(L, nm).restype = i32
             getattr(L, nm).argtypes = common + [i32, vp, vp]
@@ -123,11 +125,15 @@ def _prep(q, k, v, query_start_loc, seq_lens, block_table, H, Hkv, bs):
 
 
 def attention(q, k, v, query_start_loc, seq_lens=None, block_table=None, *, scale, causal=True,
-              k_scale=1.0, v_scale=1.0, rows=None, nthreads=0):
+              k_scale=1.0, v_scale=1.0, rows=None, nthreads=0, window_left=-1, softcap=0.0, sinks=None):
     """Definition of the varlen (optionally paged) attention forward.
 
     Returns (out [n_rows, H, hd] float64, lse [H, n_rows] float64). ``rows``
-    selects packed token indices to evaluate (default: all tokens)."""
+    selects packed token indices to evaluate (default: all tokens).
+    Variants: ``window_left`` >= 0 limits query position i to keys
+    j >= i - window_left; ``softcap`` > 0 maps each scaled score s to
+    softcap * tanh(s / softcap); ``sinks`` [H] adds one logit per head to the
+    softmax normaliser (no value row)."""
     q, k, v, qsl, seq_lens, bt, bt_stride, B, T, H, Hkv, hd, bs = _prep(q, k, v, query_start_loc, seq_lens,
                                                                            block_table, None, None, None)
     if rows is None:
@@ -138,10 +144,11 @@ def attention(q, k, v, query_start_loc, seq_lens=None, block_table=None, *, scal
         n = len(rows_arr)
     out = np.zeros((n, H, hd), np.float64)
     lse = np.zeros((H, n), np.float64)
-    rc = lib().or_attention(_ptr(q), _code(q), _ptr(k), _ptr(v), _code(k), float(k_scale), float(v_scale),
-                            _ptr(qsl), _ptr(seq_lens), _ptr(bt), bt_stride, B, H, Hkv, hd, bs,
-                            float(scale), int(bool(causal)), _ptr(rows_arr), n, _ptr(out), _ptr(lse),
-                            int(nthreads))
+    sk = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float64).reshape(H)
+    rc = lib().or_attention_ex(_ptr(q), _code(q), _ptr(k), _ptr(v), _code(k), float(k_scale), float(v_scale),
+                               _ptr(qsl), _ptr(seq_lens), _ptr(bt), bt_stride, B, H, Hkv, hd, bs,
+                               float(scale), int(bool(causal)), int(window_left), float(softcap), _ptr(sk),
+                               _ptr(rows_arr), n, _ptr(out), _ptr(lse), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the problem (H % Hkv != 0 or empty batch)")
     return out, lse

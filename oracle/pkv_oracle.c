@@ -209,6 +209,12 @@ typedef struct {
     int B, H, Hkv, hd, bs;
     double scale;
     int causal;
+    /* attention variants (the deep-dive page lists sliding window, logits soft
+     * cap and attention sinks among the supported variants; the readings are
+     * stated at or_attention_ex) */
+    int64_t window_left;  /* < 0: no window */
+    double softcap;       /* <= 0: no cap */
+    const double* sinks;  /* [H] or NULL */
 } or_problem;
 
 static int request_of(const or_problem* p, int64_t tok) {
@@ -240,6 +246,17 @@ static int64_t visible(const or_problem* p, int r, int64_t t) {
     return n;
 }
 
+/* first key query token (request r, local index t) may attend: with a
+ * window, key j is visible only if j >= i - window_left, where i = ctx + t is
+ * the query's position in its sequence */
+static int64_t first_visible(const or_problem* p, int r, int64_t t) {
+    if (p->window_left < 0) return 0;
+    int64_t q_len = p->qsl[r + 1] - p->qsl[r];
+    int64_t L = p->block_table ? p->seq_lens[r] : q_len;
+    int64_t lo = (L - q_len) + t - p->window_left;
+    return lo > 0 ? lo : 0;
+}
+
 /* Definition: two passes over the visible keys of one (token, head). */
 static void attend_one(const or_problem* p, int64_t tok, int h, double* s, double* qv,
                        double* out /* [hd] */, double* lse) {
@@ -247,20 +264,24 @@ static void attend_one(const or_problem* p, int64_t tok, int h, double* s, doubl
     int64_t t = tok - p->qsl[r];
     int g = h / (p->H / p->Hkv);
     int64_t n = visible(p, r, t);
+    int64_t lo = first_visible(p, r, t);
     int hd = p->hd;
+    double sink = p->sinks ? p->sinks[h] : -INFINITY;
     for (int d = 0; d < hd; ++d) qv[d] = load_elem(p->q, p->q_dtype, (tok * p->H + h) * hd + d);
     for (int d = 0; d < hd; ++d) out[d] = 0.0;
-    if (n == 0) { *lse = -INFINITY; return; }
-    double m = -INFINITY;
-    for (int64_t j = 0; j < n; ++j) {
+    if (n <= lo && sink == -INFINITY) { *lse = -INFINITY; return; }
+    double m = sink;
+    for (int64_t j = lo; j < n; ++j) {
         int64_t off = kv_offset(p, r, j, g);
         double dot = 0.0;
         for (int d = 0; d < hd; ++d) dot += qv[d] * (load_elem(p->k, p->kv_dtype, off + d) * p->k_scale);
         s[j] = p->scale * dot;
+        if (p->softcap > 0) s[j] = p->softcap * tanh(s[j] / p->softcap);
         if (s[j] > m) m = s[j];
     }
-    double z = 0.0;
-    for (int64_t j = 0; j < n; ++j) {
+    /* the sink is one more logit in the normaliser; it adds no value row */
+    double z = sink == -INFINITY ? 0.0 : exp(sink - m);
+    for (int64_t j = lo; j < n; ++j) {
         double w = exp(s[j] - m);
         z += w;
         int64_t off = kv_offset(p, r, j, g);
@@ -281,14 +302,25 @@ static int64_t max_len(const or_problem* p) {
 
 /* rows: packed token indices to evaluate (NULL => all T tokens, n_rows = T).
  * out: [n_rows, H, hd]; lse: [H, n_rows]. nthreads <= 0 => OpenMP default. */
-int or_attention(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
-                 double k_scale, double v_scale, const int32_t* qsl, const int32_t* seq_lens,
-                 const int32_t* block_table, int64_t bt_stride, int B, int H, int Hkv, int hd, int bs,
-                 double scale, int causal, const int64_t* rows, int64_t n_rows,
-                 double* out, double* lse, int nthreads) {
+/* Attention variants, the plainest reading of the deep-dive page's table of
+ * supported variants (it names them but gives no formulas):
+ *  window_left >= 0: sliding window -- query position i (= ctx + t) sees keys
+ *                    j >= i - window_left only (on top of the causal bound);
+ *  softcap > 0:      logits soft cap -- each scaled score s becomes
+ *                    softcap * tanh(s / softcap) before the softmax;
+ *  sinks != NULL:    attention sinks -- one extra logit sinks[h] per head
+ *                    joins the softmax normaliser and contributes no value:
+ *                    out = sum_j e^{s_j} v_j / (e^{sink} + sum_j e^{s_j}),
+ *                    lse = log(e^{sink} + sum_j e^{s_j}); a row with no
+ *                    visible key then has out = 0 and lse = sink. */
+int or_attention_ex(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                    double k_scale, double v_scale, const int32_t* qsl, const int32_t* seq_lens,
+                    const int32_t* block_table, int64_t bt_stride, int B, int H, int Hkv, int hd, int bs,
+                    double scale, int causal, int64_t window_left, double softcap, const double* sinks,
+                    const int64_t* rows, int64_t n_rows, double* out, double* lse, int nthreads) {
     if (H % Hkv != 0 || B <= 0) return -1;
     or_problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, qsl, seq_lens, block_table,
-                    bt_stride, B, H, Hkv, hd, bs, scale, causal};
+                    bt_stride, B, H, Hkv, hd, bs, scale, causal, window_left, softcap, sinks};
     int64_t L = max_len(&p);
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -313,6 +345,16 @@ int or_attention(const void* q, int q_dtype, const void* k, const void* v, int k
     return 0;
 }
 
+/* The plain definition (no variant). */
+int or_attention(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                 double k_scale, double v_scale, const int32_t* qsl, const int32_t* seq_lens,
+                 const int32_t* block_table, int64_t bt_stride, int B, int H, int Hkv, int hd, int bs,
+                 double scale, int causal, const int64_t* rows, int64_t n_rows,
+                 double* out, double* lse, int nthreads) {
+    return or_attention_ex(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, qsl, seq_lens, block_table, bt_stride,
+                           B, H, Hkv, hd, bs, scale, causal, -1, 0.0, NULL, rows, n_rows, out, lse, nthreads);
+}
+
 /* Number of threads OpenMP would use (for reporting). */
 int or_num_threads(void) {
 #ifdef _OPENMP
@@ -333,7 +375,7 @@ int or_attention_online(const void* q, int q_dtype, const void* k, const void* v
                         const int32_t* block_table, int64_t bt_stride, int B, int H, int Hkv, int hd, int bs,
                         double scale, int causal, int tile, double* out, double* lse) {
     or_problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, qsl, seq_lens, block_table,
-                    bt_stride, B, H, Hkv, hd, bs, scale, causal};
+                    bt_stride, B, H, Hkv, hd, bs, scale, causal, -1, 0.0, NULL};
     int64_t T = qsl[B];
     double* qv = (double*)malloc(sizeof(double) * hd);
     double* sc = (double*)malloc(sizeof(double) * tile);
@@ -388,7 +430,7 @@ int or_attention_online_normalised(const void* q, int q_dtype, const void* k, co
                                    const int32_t* block_table, int64_t bt_stride, int B, int H, int Hkv, int hd,
                                    int bs, double scale, int causal, int tile, double* out, double* lse) {
     or_problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, qsl, seq_lens, block_table,
-                    bt_stride, B, H, Hkv, hd, bs, scale, causal};
+                    bt_stride, B, H, Hkv, hd, bs, scale, causal, -1, 0.0, NULL};
     int64_t T = qsl[B];
     double* qv = (double*)malloc(sizeof(double) * hd);
     double* sc = (double*)malloc(sizeof(double) * tile);
@@ -446,7 +488,7 @@ int or_attention_split(const void* q, int q_dtype, const void* k, const void* v,
                        const int32_t* block_table, int64_t bt_stride, int B, int H, int Hkv, int hd, int bs,
                        double scale, int causal, int64_t seg_len, double* out, double* lse) {
     or_problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, qsl, seq_lens, block_table,
-                    bt_stride, B, H, Hkv, hd, bs, scale, causal};
+                    bt_stride, B, H, Hkv, hd, bs, scale, causal, -1, 0.0, NULL};
     int64_t T = qsl[B];
     int64_t L = max_len(&p);
     int64_t S = (L + seg_len - 1) / seg_len;

@@ -17,10 +17,16 @@ def decode(a: np.ndarray, e4m3_table=None) -> np.ndarray:
     raise TypeError(a.dtype)
 
 
-def global_attention(q, k_flat, v_flat, q_start, kv_start, *, scale, causal, H, Hkv):
+def global_attention(q, k_flat, v_flat, q_start, kv_start, *, scale, causal, H, Hkv, window_left=-1,
+                     softcap=0.0, sinks=None):
     """q: [T, H, hd]; k_flat/v_flat: [sum L, Hkv, hd] packed per request in
     position order; q_start [B+1], kv_start [B+1]. Returns out [T, H, hd],
-    lse [H, T] (natural log)."""
+    lse [H, T] (natural log).
+
+    Variants: a window keeps, for the query at sequence position i, only keys
+    at positions >= i - window_left; a soft cap maps scores through
+    softcap * tanh(s / softcap); a sink is one more column of the global
+    matrix, visible to every query of its head, with a zero value row."""
     qd, kd, vd = decode(q), decode(k_flat), decode(v_flat)
     T = qd.shape[0]
     N = kd.shape[0]
@@ -34,19 +40,28 @@ def global_attention(q, k_flat, v_flat, q_start, kv_start, *, scale, causal, H, 
         for t in range(qn):
             n = (ctx + t + 1) if causal else L
             n = max(0, min(n, L))
-            allowed[q0 + t, k0:k0 + n] = True
+            lo = max(0, ctx + t - window_left) if window_left >= 0 else 0
+            if n > lo:
+                allowed[q0 + t, k0 + lo:k0 + n] = True
     g = H // Hkv
     out = np.zeros((T, H, qd.shape[2]))
     lse = np.full((H, T), -np.inf)
+    hd = qd.shape[2]
     for h in range(H):
         S = scale * (qd[:, h, :] @ kd[:, h // g, :].T)          # [T, N] global matrix
+        if softcap > 0:
+            S = softcap * np.tanh(S / softcap)
         S = np.where(allowed, S, -np.inf)
+        Vh = vd[:, h // g, :]
+        if sinks is not None:                                    # the sink column and its zero value row
+            S = np.concatenate([S, np.full((T, 1), float(sinks[h]))], axis=1)
+            Vh = np.concatenate([Vh, np.zeros((1, hd))], axis=0)
         m = S.max(axis=1, keepdims=True)
         has = np.isfinite(m[:, 0])
         m = np.where(np.isfinite(m), m, 0.0)
         P = np.exp(S - m)
         z = P.sum(axis=1, keepdims=True)
-        O = (P @ vd[:, h // g, :]) / np.where(z > 0, z, 1.0)
+        O = (P @ Vh) / np.where(z > 0, z, 1.0)
         out[:, h, :] = np.where(has[:, None], O, 0.0)
         lse[h] = np.where(has, m[:, 0] + np.log(np.where(z[:, 0] > 0, z[:, 0], 1.0)), -np.inf)
     return out, lse

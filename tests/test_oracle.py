@@ -495,3 +495,119 @@ def test_generator_slots_consistent_with_block_table():
     for r in range(prob.B):
         for pos in range(int(prob.seq_lens[r])):
             assert oracle.slot(prob.block_table, r, pos, prob.bs) == prob.kv_slots[prob.pos_rows[r][pos]]
+
+
+# ------------------------------------------------- attention variants (window, soft cap, sinks)
+
+VARIANT_CASES = [
+    dict(window_left=3, softcap=0.0, sinks=False),
+    dict(window_left=0, softcap=0.0, sinks=False),
+    dict(window_left=-1, softcap=2.0, sinks=False),
+    dict(window_left=-1, softcap=0.0, sinks=True),
+    dict(window_left=5, softcap=1.5, sinks=True),
+]
+
+
+def _variant_problem(seed=46):
+    return workloads.make_problem(seed, [5, 1, 9, 3], [3, 11, 0, 20], H=4, Hkv=2, hd=16, bs=4)
+
+
+def _sinks(prob, seed=7):
+    return np.random.default_rng(seed).standard_normal(prob.H) * 2.0
+
+
+def _oracle_variant(prob, causal, **kw):
+    kc, vc = prob.empty_cache()
+    kc, vc = oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc, vc, prob.kv_slots, prob.bs)
+    return oracle.attention(prob.q, kc, vc, prob.query_start_loc, prob.seq_lens, prob.block_table,
+                            scale=prob.scale, causal=causal, **kw)
+
+
+@pytest.mark.parametrize("var", VARIANT_CASES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_variants_match_global_matrix_brute_force(var, causal):
+    prob = _variant_problem()
+    sinks = _sinks(prob) if var["sinks"] else None
+    out, lse = _oracle_variant(prob, causal, window_left=var["window_left"], softcap=var["softcap"], sinks=sinks)
+    kf, vf, loc = prob.flat_kv()
+    b_out, b_lse = global_attention(prob.q, kf, vf, prob.query_start_loc, loc, scale=prob.scale, causal=causal,
+                                    H=prob.H, Hkv=prob.Hkv, window_left=var["window_left"], softcap=var["softcap"],
+                                    sinks=sinks)
+    np.testing.assert_allclose(out, b_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, b_lse, rtol=0, atol=1e-12)
+
+
+def test_window_wider_than_sequence_is_no_window():
+    prob = _variant_problem(47)
+    a = _oracle_variant(prob, True)
+    b = _oracle_variant(prob, True, window_left=int(prob.seq_lens.max()))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_window_zero_sees_only_itself():
+    """Causal with window_left = 0: each query sees exactly its own key, so the
+    output is its own V row and lse its own score."""
+    prob = _variant_problem(48)
+    out, lse = _oracle_variant(prob, True, window_left=0)
+    q = workloads.storage_to_f32(prob.q).astype(np.float64)
+    k = workloads.storage_to_f32(prob.kv_src_k).astype(np.float64)
+    v = workloads.storage_to_f32(prob.kv_src_v).astype(np.float64)
+    g = prob.H // prob.Hkv
+    for tok in range(prob.T):
+        row = prob.new_rows[tok]
+        for h in range(prob.H):
+            np.testing.assert_allclose(out[tok, h], v[row, h // g], rtol=0, atol=1e-15)
+            np.testing.assert_allclose(lse[h, tok], prob.scale * q[tok, h] @ k[row, h // g], rtol=0, atol=1e-12)
+
+
+def test_sinks_relation_to_plain_attention():
+    """A sink only enlarges the normaliser: lse' = logaddexp(lse, sink) and
+    out' = out * exp(lse - lse'); a sink of -inf changes nothing."""
+    prob = _variant_problem(49)
+    sinks = _sinks(prob, 9)
+    out, lse = _oracle_variant(prob, True)
+    out_s, lse_s = _oracle_variant(prob, True, sinks=sinks)
+    want_lse = np.logaddexp(lse, sinks[:, None])
+    np.testing.assert_allclose(lse_s, want_lse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out_s, out * np.exp(lse - want_lse).T[:, :, None], rtol=0, atol=1e-12)
+    out_n, lse_n = _oracle_variant(prob, True, sinks=np.full(prob.H, -np.inf))
+    assert np.array_equal(out_n, out) and np.array_equal(lse_n, lse)
+
+
+def test_sink_with_no_visible_key():
+    """A row that sees no key keeps out = 0 and takes lse = its sink (here
+    every row: non-causal over zero cached keys)."""
+    prob = workloads.make_problem(50, [3], [5], H=2, Hkv=1, hd=8, bs=2)
+    sinks = np.array([0.25, -1.5])
+    kc, vc = prob.empty_cache()
+    kc, vc = oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc, vc, prob.kv_slots, prob.bs)
+    no_keys = np.zeros_like(prob.seq_lens)
+    out0, lse0 = oracle.attention(prob.q, kc, vc, prob.query_start_loc, no_keys, prob.block_table,
+                                  scale=prob.scale, causal=False, sinks=sinks)
+    assert np.all(out0 == 0.0)
+    np.testing.assert_array_equal(lse0, np.repeat(sinks[:, None], prob.T, axis=1))
+
+
+def test_softcap_single_key_closed_form():
+    """The first query of a request without context sees one key: out = that
+    V row, lse = softcap * tanh(scale * q.k / softcap)."""
+    prob = workloads.make_problem(51, [4, 2], [0, 0], H=2, Hkv=2, hd=16, bs=4)
+    out, lse = _oracle_variant(prob, True, softcap=0.75)
+    q = workloads.storage_to_f32(prob.q).astype(np.float64)
+    k = workloads.storage_to_f32(prob.kv_src_k).astype(np.float64)
+    v = workloads.storage_to_f32(prob.kv_src_v).astype(np.float64)
+    for r in range(prob.B):
+        tok = prob.query_start_loc[r]
+        row = prob.new_rows[tok]
+        for h in range(prob.H):
+            s = prob.scale * q[tok, h] @ k[row, h]
+            np.testing.assert_allclose(out[tok, h], v[row, h], rtol=0, atol=1e-15)
+            np.testing.assert_allclose(lse[h, tok], 0.75 * math.tanh(s / 0.75), rtol=0, atol=1e-12)
+
+
+def test_huge_softcap_approaches_no_cap():
+    prob = _variant_problem(52)
+    a = _oracle_variant(prob, True)
+    b = _oracle_variant(prob, True, softcap=1e7)
+    np.testing.assert_allclose(b[0], a[0], rtol=0, atol=1e-9)
+    np.testing.assert_allclose(b[1], a[1], rtol=0, atol=1e-9)

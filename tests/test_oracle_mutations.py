@@ -1,6 +1,7 @@
 """The oracle's pins must catch plausible mistakes: each test below plants one
 mistake in a copy of the oracle's C source (a dropped term, a wrong sign,
-index or base, an off-by-one, a transposed operand, a wrong rounding rule),
+index or base, an off-by-one, a transposed operand, a wrong rounding rule,
+a mistake in a variant: window bound, soft cap, sink),
 builds the copy into a temporary library, and runs the pin suite
 (tests/test_oracle.py) against it in a subprocess; the suite must fail. A
 control run on an unmodified copy must pass. Nothing here touches the GPU or
@@ -32,6 +33,10 @@ MUTANTS = {
     "k_operand_reversed": [("dot += qv[d] * (load_elem(p->k, p->kv_dtype, off + d) * p->k_scale);",
                             "dot += qv[d] * (load_elem(p->k, p->kv_dtype, off + (hd - 1 - d)) * p->k_scale);")],
     "drop_v_scale": [("(load_elem(p->v, p->kv_dtype, off + d) * p->v_scale)", "load_elem(p->v, p->kv_dtype, off + d)")],
+    "window_off_by_one": [("int64_t lo = (L - q_len) + t - p->window_left;",
+                           "int64_t lo = (L - q_len) + t - p->window_left + 1;")],
+    "softcap_no_division": [("s[j] = p->softcap * tanh(s[j] / p->softcap);", "s[j] = p->softcap * tanh(s[j]);")],
+    "sink_dropped": [("double z = sink == -INFINITY ? 0.0 : exp(sink - m);", "double z = 0.0;")],
 }
 
 
