@@ -13,7 +13,10 @@ heads, head size 128, bf16), batch 64, one query token per request, context
 lengths uniform in [512, 4096], page size 16, random block table. The metric is
 KV bytes read per second (GB/s) against the MI355X HBM peak of 8 TB/s.
 Other workloads (--workload): chunked_prefill (TFLOP/s against the 2.5 PFLOP/s
-bf16 dense MFMA peak), long_decode, long_decode_cascade, fp8_decode.
+bf16 dense MFMA peak), long_decode, long_decode_cascade, fp8_decode. The
+attention variants can be switched on for any workload but the cascade
+(--sliding-window W, --softcap C, --sinks); bytes and flops then count only
+what the window leaves visible.
 
 Prints ONE JSON line. The float64 CPU oracle is timed on the same workload
 (rank 0, one GPU only) as a reported baseline.
@@ -78,14 +81,35 @@ def kv_elem_bytes(prob):
     return 1 if prob.cache_dtype == "fp8" else 2
 
 
-def kv_bytes(prob, unique=False):
-    """Algorithmic KV bytes of one forward: every request reads K and V of all
-    its seq_len positions (cascade: the shared prefix once)."""
+def kv_bytes(prob, unique=False, window=0):
+    """Algorithmic KV bytes of one forward: every request with a query token
+    reads K and V of all its seq_len positions (cascade: the shared prefix
+    once); with a sliding
+    window of w keys, of the positions its first query token's window starts
+    at onward."""
     per_tok = prob.Hkv * prob.hd * 2 * kv_elem_bytes(prob)
-    toks = int(prob.seq_lens.sum())
+    L = np.where(prob.q_lens > 0, prob.seq_lens, 0).astype(np.int64)  # a request without queries reads nothing
+    if window > 0:
+        toks = int((L - np.minimum(L, np.maximum(0, prob.ctx_lens.astype(np.int64) - (window - 1)))).sum())
+    else:
+        toks = int(L.sum())
     if unique and prob.shared_prefix:
         toks -= (prob.B - 1) * prob.shared_prefix
     return toks * per_tok
+
+
+def visible_keys(prob, window=0):
+    """Keys each packed query row sees: ctx + t + 1 (causal) or L, at most
+    the window."""
+    n = []
+    for r in range(prob.B):
+        ql, ctx, L = int(prob.q_lens[r]), int(prob.ctx_lens[r]), int(prob.seq_lens[r])
+        i = ctx + np.arange(ql, dtype=np.int64)
+        vis = i + 1 if prob.causal else np.full(ql, L, np.int64)
+        if window > 0:
+            vis = vis - np.maximum(0, i - (window - 1))
+        n.append(vis)
+    return np.concatenate(n) if n else np.zeros(0, np.int64)
 
 
 def kernel_sources_hash():
@@ -137,12 +161,10 @@ def pmc_summary(args):
           f"  # copy factors fetch {f_fac:.4f} write {w_fac:.4f}")
 
 
-def visible_flops(prob):
-    """4 * hd * H * (visible query-key pairs): QK^T and PV, causal pairs only."""
-    ql = prob.q_lens.astype(np.int64)
-    ctx = prob.ctx_lens.astype(np.int64)
-    pairs = int((ql * ctx + ql * (ql + 1) // 2).sum()) if prob.causal else int((ql * prob.seq_lens).sum())
-    return 4 * prob.hd * prob.H * pairs
+def visible_flops(prob, window=0):
+    """4 * hd * H * (visible query-key pairs): QK^T and PV, causal (and
+    in-window) pairs only."""
+    return 4 * prob.hd * prob.H * int(visible_keys(prob, window).sum())
 
 
 def main():
@@ -156,6 +178,9 @@ def main():
     ap.add_argument("--heads", type=int, default=0, help="paged_decode: query heads (default 32)")
     ap.add_argument("--kv-heads", type=int, default=0, help="paged_decode: kv heads (default 8)")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--sliding-window", type=int, default=0, help="a query sees at most this many keys (0: off)")
+    ap.add_argument("--softcap", type=float, default=0.0, help="logits soft cap (0: off)")
+    ap.add_argument("--sinks", action="store_true", help="one sink logit per query head (seeded)")
     ap.add_argument("--replicas", type=int, default=0, help="KV cache copies used in turn (0 = enough for 1.5 GB)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: the timed steps are one captured HIP graph)")
@@ -200,6 +225,9 @@ def main():
         if a.dtype == np.uint8:
             return torch.from_numpy(a).to(dev).view(torch.float8_e4m3fn)
         return torch.from_numpy(a).to(dev)
+    variants = args.sliding_window > 0 or args.softcap > 0 or args.sinks
+    if variants and args.workload == "long_decode_cascade":
+        raise SystemExit("bench: the attention variants are not benchmarked on the cascade workload")
     t0 = time.time()
     over = {k: v for k, v in (("B", args.batch), ("H", args.heads), ("Hkv", args.kv_heads)) if v}
     prob = make(args.workload, args.block_size, over)
@@ -238,13 +266,16 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty((prob.H, prob.T), dtype=torch.float32, device=dev)
     cascade = prob.shared_prefix > 0
-    fwd_kw = dict(softmax_scale=prob.scale, causal=prob.causal, k_scale=ks, v_scale=vs)
+    W = args.sliding_window
+    sinks_h = np.random.default_rng(12345).normal(1.5, 2.0, prob.H).astype(np.float32) if args.sinks else None
+    fwd_kw = dict(softmax_scale=prob.scale, causal=prob.causal, k_scale=ks, v_scale=vs, sliding_window=W,
+                  softcap=args.softcap, sinks=None if sinks_h is None else to_dev(sinks_h))
     if not cascade:
         need = pkv.pkv_varlen_workspace_size(q, reps[0][0], reps[0][1], qsl, seq_lens, bt, prob.max_seqlen_q,
-                                             prob.max_seqlen_k, prob.scale, prob.causal, args.num_splits)
+                                             prob.max_seqlen_k, prob.scale, prob.causal, args.num_splits, W)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         splits = pkv.pkv_varlen_num_splits(q, reps[0][0], reps[0][1], qsl, seq_lens, bt, prob.max_seqlen_q,
-                                           prob.max_seqlen_k, prob.scale, prob.causal, args.num_splits)
+                                           prob.max_seqlen_k, prob.scale, prob.causal, args.num_splits, W)
     else:
         splits = None
 
@@ -299,9 +330,9 @@ def main():
     decode_like = args.workload != "chunked_prefill"
     # HBM bytes per launch of the dominant kernel from committed counter runs
     # (None unless they were taken on the current kernel sources)
-    traffic = measured_traffic(args.workload, prob.bs)
+    traffic = None if variants else measured_traffic(args.workload, prob.bs)
     if decode_like:
-        kvb = kv_bytes(prob, unique=cascade)
+        kvb = kv_bytes(prob, unique=cascade, window=W)
         value = kvb / (ms_step * 1e-3) / 1e9
         metric, unit = "paged decode KV GB/s", "GB/s"
         # the dominant kernel is the attention kernel; per step it reads the
@@ -311,7 +342,7 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "algorithmic_bytes_per_launch": kvb}
     else:
-        fl = visible_flops(prob)
+        fl = visible_flops(prob, W)
         value = fl / (ms_step * 1e-3) / 1e12
         metric, unit = "causal prefill TFLOP/s", "TFLOP/s"
         achieved = fl / (main_ms / args.steps * 1e-3) / 1e12
@@ -331,9 +362,11 @@ def main():
         kc_o, vc_o = prob.empty_cache()
         kc_o, vc_o = oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc_o, vc_o, prob.kv_slots, prob.bs,
                                         k_scale=prob.k_scale, v_scale=prob.v_scale)
+        var_o = dict(window_left=W - 1 if W > 0 else -1, softcap=args.softcap,
+                     sinks=None if sinks_h is None else sinks_h.astype(np.float64))
         ref, ref_lse = oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, prob.seq_lens, prob.block_table,
                                         scale=prob.scale, causal=prob.causal, rows=sample, k_scale=prob.k_scale,
-                                        v_scale=prob.v_scale)
+                                        v_scale=prob.v_scale, **var_o)
         tol = 5e-2 if prob.cache_dtype == "fp8" else 1e-2
         o = out.float().cpu().numpy().astype(np.float64)[sample]
         half_ulp = np.where(np.abs(ref) > 0, np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8), 0)
@@ -349,21 +382,18 @@ def main():
         nthr = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
         # rows in packed order, a few at a time, until about --cpu-seconds
         done_rows, done_bytes, done_flops, t_cpu = 0, 0, 0, 0.0
-        req_of = np.searchsorted(prob.query_start_loc, np.arange(prob.T), side="right") - 1
+        vis = visible_keys(prob, W)
         per_tok_kv = prob.Hkv * prob.hd * 2 * kv_elem_bytes(prob)
         for r0 in range(0, prob.T, 16):
             rows = np.arange(r0, min(prob.T, r0 + 16))
             t1 = time.perf_counter()
             oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, prob.seq_lens, prob.block_table,
                              scale=prob.scale, causal=prob.causal, rows=rows, k_scale=prob.k_scale,
-                             v_scale=prob.v_scale, nthreads=nthr)
+                             v_scale=prob.v_scale, nthreads=nthr, **var_o)
             t_cpu += time.perf_counter() - t1
-            for tok in rows:
-                r = req_of[tok]
-                t_loc = tok - prob.query_start_loc[r]
-                n_vis = int(prob.ctx_lens[r]) + t_loc + 1 if prob.causal else int(prob.seq_lens[r])
-                done_flops += 4 * prob.hd * prob.H * n_vis
-                done_bytes += n_vis * per_tok_kv   # keys read for this row (all kv heads)
+            n_vis = int(vis[rows].sum())
+            done_flops += 4 * prob.hd * prob.H * n_vis
+            done_bytes += n_vis * per_tok_kv   # keys read for these rows (all kv heads)
             done_rows += len(rows)
             if t_cpu >= args.cpu_seconds:
                 break
@@ -378,6 +408,12 @@ def main():
     if over or (args.block_size and args.workload == "paged_decode"):
         desc = (f"paged decode, {prob.H}/{prob.Hkv} heads, head {prob.hd}, bf16, batch {prob.B}, "
                 f"ctx U[512,4096], page {prob.bs}")
+    if W > 0:
+        desc += f", sliding window {W}"
+    if args.softcap > 0:
+        desc += f", softcap {args.softcap:g}"
+    if args.sinks:
+        desc += ", sinks"
     cfg = {"workload": desc, "global_batch": prob.B, "seq_len": prob.max_seqlen_k,
            "num_heads": prob.H, "num_kv_heads": prob.Hkv, "head_size": prob.hd, "block_size": prob.bs,
            "kv_cache_dtype": prob.cache_dtype, "num_splits": splits, "cache_replicas": R,

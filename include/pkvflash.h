@@ -97,6 +97,23 @@ pkv_status pkv_cache_write(const void* key, const void* value, pkv_dtype src_dty
  *   out[t][h] = sum_j softmax_j(softmax_scale * q[t][h] . k_j) v_j
  *   lse[h][t] = log(sum_j exp(softmax_scale * q[t][h] . k_j))   (natural log)
  * A row with no visible key gets out = 0 and lse = -inf.
+ * Variants (the deep-dive page's table of supported variants names a sliding
+ * window, a logits soft cap and attention sinks without formulas; these are
+ * the plainest readings, each off by default):
+ *   sliding_window > 0: the query at position i = ctx_r + t sees only the
+ *          keys j >= i - (sliding_window - 1), at most sliding_window keys
+ *          ending at its own position (on top of the causal bound); 0: no
+ *          window (the zero of a cleared struct). KV tiles wholly before
+ *          every query's window are not read.
+ *   softcap > 0: each scaled score s becomes softcap * tanh(s / softcap)
+ *          before the softmax; 0: no cap.
+ *   sinks != NULL: sinks[h] (device fp32, [num_heads], natural-log units) is
+ *          one more logit in head h's softmax normaliser that contributes no
+ *          value row: out = sum_j e^{s_j} v_j / (e^{sink} + sum_j e^{s_j}) and
+ *          lse = log(e^{sink} + sum_j e^{s_j}); a row with no visible key then
+ *          gets out = 0, lse = sinks[h]. Split partials exclude the sink and
+ *          the merge adds it once (a cascade passes sinks to one of its two
+ *          forward calls only).
  *
  * Layouts: q, out [num_tokens, num_heads, head_size] in q_dtype (out has the
  *          type of q); lse [num_heads, num_tokens] fp32, or NULL;
@@ -145,6 +162,10 @@ typedef struct pkv_varlen_args {
     int32_t q_dtype;        /* pkv_dtype */
     int32_t kv_dtype;       /* pkv_dtype */
     float softmax_scale;
+    /* attention variants (see above) */
+    int32_t sliding_window; /* 0: no sliding window */
+    float softcap;          /* 0: no logits soft cap */
+    const float* sinks;     /* [num_heads] device fp32, or NULL */
 } pkv_varlen_args;
 
 /* sizeof(pkv_varlen_args), so bindings can check their mirror of the struct. */

@@ -60,6 +60,9 @@ class pkv_varlen_args(ctypes.Structure):
         ("q_dtype", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("sliding_window", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
+        ("sinks", ctypes.c_void_p),
     ]
 
 
@@ -160,8 +163,11 @@ def pkv_cache_write(key, value, k_cache, v_cache, slot_mapping, k_scale=None, v_
 
 
 def _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
-                 softmax_scale, causal, out, lse, k_scale, v_scale, num_splits, workspace):
-    _contig(q, k_cache, v_cache, query_start_loc, seq_lens, out, lse, workspace)
+                 softmax_scale, causal, out, lse, k_scale, v_scale, num_splits, workspace, sliding_window=0,
+                 softcap=0.0, sinks=None):
+    _contig(q, k_cache, v_cache, query_start_loc, seq_lens, out, lse, workspace, sinks)
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != q.shape[1]):
+        raise ValueError("sinks must be a float32 tensor of num_heads elements")
     T, H, hd = q.shape
     a = pkv_varlen_args()
     a.q, a.k_cache, a.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
@@ -190,22 +196,25 @@ def _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, ma
     a.causal = 1 if causal else 0
     a.q_dtype, a.kv_dtype = _dtype_code(q), _dtype_code(k_cache)
     a.softmax_scale = float(softmax_scale)
+    a.sliding_window = int(sliding_window)
+    a.softcap = float(softcap)
+    a.sinks = _ptr(sinks)
     return a
 
 
 def pkv_varlen_workspace_size(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q,
-                              max_seqlen_k, softmax_scale, causal=True, num_splits=0):
+                              max_seqlen_k, softmax_scale, causal=True, num_splits=0, sliding_window=0):
     a = _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
-                     softmax_scale, causal, None, None, None, None, num_splits, None)
+                     softmax_scale, causal, None, None, None, None, num_splits, None, sliding_window)
     if lib().pkv_varlen_num_splits(ctypes.byref(a)) == 0:
         _check(lib().pkv_varlen_check(ctypes.byref(a)))
     return int(lib().pkv_varlen_workspace_size(ctypes.byref(a)))
 
 
 def pkv_varlen_num_splits(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q,
-                          max_seqlen_k, softmax_scale, causal=True, num_splits=0):
+                          max_seqlen_k, softmax_scale, causal=True, num_splits=0, sliding_window=0):
     a = _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
-                     softmax_scale, causal, None, None, None, None, num_splits, None)
+                     softmax_scale, causal, None, None, None, None, num_splits, None, sliding_window)
     n = int(lib().pkv_varlen_num_splits(ctypes.byref(a)))
     if n == 0:
         _check(lib().pkv_varlen_check(ctypes.byref(a)))
@@ -214,10 +223,12 @@ def pkv_varlen_num_splits(q, k_cache, v_cache, query_start_loc, seq_lens, block_
 
 def pkv_varlen_fwd(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
                    softmax_scale, causal=True, out=None, lse=None, k_scale=None, v_scale=None, num_splits=0,
-                   workspace=None, return_lse=False, stream=None):
+                   workspace=None, return_lse=False, stream=None, sliding_window=0, softcap=0.0, sinks=None):
     """Varlen attention forward. q [T, H, hd]; paged caches [num_blocks, bs, Hkv, hd] with block_table
     [B, >= ceil(max_seqlen_k / bs)] int32 (a column slice of a larger table is fine), or flat caches
-    [T, Hkv, hd] with block_table None. Returns out (and lse [H, T] fp32 when requested)."""
+    [T, Hkv, hd] with block_table None. Returns out (and lse [H, T] fp32 when requested).
+    Variants: sliding_window (a query sees at most this many keys, ending at its own position; 0: none),
+    softcap (0: none), sinks (float32 [H] on the device, or None)."""
     T, H, hd = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -225,11 +236,13 @@ def pkv_varlen_fwd(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, 
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     if workspace is None and num_splits != 1:
         need = pkv_varlen_workspace_size(q, k_cache, v_cache, query_start_loc, seq_lens, block_table,
-                                         max_seqlen_q, max_seqlen_k, softmax_scale, causal, num_splits)
+                                         max_seqlen_q, max_seqlen_k, softmax_scale, causal, num_splits,
+                                         sliding_window)
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a = _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
-                     softmax_scale, causal, out, lse, k_scale, v_scale, num_splits, workspace)
+                     softmax_scale, causal, out, lse, k_scale, v_scale, num_splits, workspace, sliding_window, softcap,
+                     sinks)
     _check(lib().pkv_varlen_fwd(ctypes.byref(a), _stream(stream)))
     return (out, lse) if return_lse else out
 
@@ -246,11 +259,12 @@ def pkv_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suff
 
 def cascade_attention(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, common_prefix_len,
                       max_seqlen_q, max_seqlen_k, softmax_scale, k_scale=None, v_scale=None, out=None,
-                      return_lse=False, stream=None):
+                      return_lse=False, stream=None, softcap=0.0, sinks=None):
     """Shared-prefix attention as three library calls (deep-dive page, cascade attention section):
     every query against the common prefix (non-causal, first block-table row), each request against
     its own suffix (causal, the block table past the prefix blocks), then the log-sum-exp merge.
-    common_prefix_len must be a multiple of the block size."""
+    common_prefix_len must be a multiple of the block size. A soft cap applies to both passes; sinks
+    enter the suffix pass only, so the merged normaliser counts them once."""
     T, H, hd = q.shape
     bs = k_cache.shape[1]
     if common_prefix_len % bs:
@@ -261,10 +275,11 @@ def cascade_attention(q, k_cache, v_cache, query_start_loc, seq_lens, block_tabl
     prefix_len = torch.tensor([common_prefix_len], dtype=torch.int32, device=dev)
     o_p, l_p = pkv_varlen_fwd(q, k_cache, v_cache, prefix_qsl, prefix_len, block_table[:1], T, common_prefix_len,
                               softmax_scale, causal=False, k_scale=k_scale, v_scale=v_scale, return_lse=True,
-                              stream=stream)
+                              stream=stream, softcap=softcap)
     o_s, l_s = pkv_varlen_fwd(q, k_cache, v_cache, query_start_loc, seq_lens - common_prefix_len,
                               block_table[:, nblk:], max_seqlen_q, max_seqlen_k - common_prefix_len, softmax_scale,
-                              causal=True, k_scale=k_scale, v_scale=v_scale, return_lse=True, stream=stream)
+                              causal=True, k_scale=k_scale, v_scale=v_scale, return_lse=True, stream=stream,
+                              softcap=softcap, sinks=sinks)
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty((H, T), dtype=torch.float32, device=dev) if return_lse else None

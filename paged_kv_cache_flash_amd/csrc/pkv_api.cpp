@@ -83,6 +83,9 @@ pkv_status validate_sizes(const pkv_varlen_args* a) {
                           (a->q_dtype == PKV_F32 && a->kv_dtype == PKV_F32);
     if (!ok_types) return fail(PKV_ERR_UNSUPPORTED, "unsupported (q_dtype, kv_dtype) = (%d, %d)", a->q_dtype, a->kv_dtype);
     if (!std::isfinite(a->softmax_scale)) return fail(PKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (a->sliding_window < 0) return fail(PKV_ERR_INVALID_ARG, "sliding_window must be >= 0 (0: no window)");
+    if (!(a->softcap >= 0.f) || !std::isfinite(a->softcap))
+        return fail(PKV_ERR_INVALID_ARG, "softcap must be finite and >= 0 (0: off)");
     if (a->num_splits < 0 || a->num_splits > 256) return fail(PKV_ERR_INVALID_ARG, "num_splits must be in [0, 256]");
     if (a->num_tokens == 0) return ok();
     if (a->num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_seqs must be <= 65535");
@@ -115,7 +118,12 @@ Plan make_plan(const pkv_varlen_args* a) {
     Plan pl{};
     const int g = a->num_heads / a->num_kv_heads;
     const bool paged = a->block_table != nullptr;
-    const int64_t max_k = paged ? a->max_seqlen_k : a->max_seqlen_q;
+    int64_t max_k = paged ? a->max_seqlen_k : a->max_seqlen_q;
+    // With a sliding window a request's keys start at its window base (the
+    // window start of its first query token, rounded down to 64 keys), so
+    // the splits only need to cover the span from there to its last key.
+    if (a->sliding_window > 0)
+        max_k = std::min<int64_t>(max_k, (int64_t)a->sliding_window - 1 + a->max_seqlen_q + 63);
     const bool mfma = a->q_dtype == PKV_BF16 && mfma_head(a->head_size) && g <= kPrefillMaxGroup;
     int64_t items;
     int align;
@@ -251,6 +259,10 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     p.n_qtiles = pl.n_qtiles;
     p.causal = a->causal ? 1 : 0;
     p.scale_log2 = a->softmax_scale * 1.4426950408889634f;  // log2(e): kernels use exp2
+    p.window_left = a->sliding_window - 1;  // -1: none
+    p.softcap_l2 = a->softcap > 0.f ? a->softcap * 1.4426950408889634f : 0.f;
+    p.softcap_inv2 = a->softcap > 0.f ? 2.f / a->softcap : 0.f;
+    p.sinks = a->sinks;
     if (pl.kind == Kind::DecodeBalanced) {
         const int64_t slots = balanced_waves(a) + (int64_t)a->num_seqs * a->num_kv_heads;
         p.sk_waves = (int32_t)balanced_waves(a);

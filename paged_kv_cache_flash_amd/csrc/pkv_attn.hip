@@ -96,6 +96,55 @@ __device__ __forceinline__ int request_of(const int32_t* qsl, int B, int64_t tok
     return lo;
 }
 
+// Sliding window: the first key query position `pos` (its index among the
+// request's keys) may see.
+__device__ __forceinline__ int window_lo(const FwdParams& p, int pos) {
+    return p.window_left < 0 ? 0 : max(0, pos - p.window_left);
+}
+
+// Where a request's KV ranges start: the window start of its first query
+// token (no later token sees an earlier key), rounded down to 64 keys; 0
+// without a window. Split s of a request covers keys
+// [base + s * split_len, base + (s+1) * split_len), and the balanced decode
+// list holds the request's 32-key tiles from base on.
+__device__ __forceinline__ int window_base(const FwdParams& p, int q_len, int L) {
+    return window_lo(p, L - q_len) & ~63;
+}
+
+// Logits soft cap in the log2 domain: x = s * log2(e) becomes
+// cap_l2 * tanh(x / cap_l2) with cap_l2 = softcap * log2(e), computed as
+// cap_l2 * (1 - 2 / (e^{2 s / softcap} + 1)) and e^{2 s / softcap} =
+// exp2(x * cap_inv2), cap_inv2 = 2 / softcap. Saturates to +-cap_l2.
+__device__ __forceinline__ float softcap_l2(float x, float cap_l2, float cap_inv2) {
+    const float e = fast_exp2(x * cap_inv2);
+    return cap_l2 * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
+}
+
+// Sink logit of query head h in the log2 domain (-inf without sinks).
+__device__ __forceinline__ float sink_l2(const FwdParams& p, int h) {
+    return p.sinks ? p.sinks[h] * kLog2e : -INFINITY;
+}
+
+// Final normalisation of one row: m is the log2-domain maximum the running
+// sum l and the accumulator are taken against, vsc the value scale. Returns
+// the factor that turns the accumulator into the output, and the row's lse
+// (natural log). A sink logit (log2 domain; -inf: none) joins the normaliser
+// and adds no value: factor = vsc / (l + 2^(sink - m)), with both terms taken
+// against max(m, sink) so neither can overflow.
+__device__ __forceinline__ void finalize_row(float m, float l, float sink2, float vsc, float& factor, float& lse) {
+    if (sink2 == -INFINITY) {
+        factor = l > 0.f ? vsc / l : 0.f;
+        const float mu = m == -INFINITY ? 0.f : m;
+        lse = l > 0.f ? (mu + fast_log2(l)) * kLn2 : -INFINITY;
+    } else {
+        const float mu = fmaxf(m, sink2);
+        const float a = l > 0.f ? fast_exp2(m - mu) : 0.f;
+        const float lt = l * a + fast_exp2(sink2 - mu);
+        factor = vsc * a / lt;
+        lse = (mu + fast_log2(lt)) * kLn2;
+    }
+}
+
 // ----------------------------------------------------------------- decode
 
 // One decode wave's 32-key tile: loads, LDS staging and compute. The LDS area
@@ -164,12 +213,15 @@ struct DecodeTile {
         wave_lds_sync();
     }
     // One tile from LDS: S^T with K as the A operand and the item's query
-    // rows as the 16 columns, masking keys at or past `limit` (per row),
+    // rows as the 16 columns, masking keys at or past `limit` (per row) and,
+    // with the variants compiled in (VAR), keys before `lo` and applying the
+    // soft cap (cap_l2 > 0),
     // online softmax, then O^T += V^T P^T with V^T read transposed. m_run is
     // row-uniform (log2 domain), l_run per lane (this lane's keys only).
-    static __device__ __forceinline__ void compute(const uint16_t* stage, int lane, int t0, int limit, float sl2,
-                                                   const u32x4 (&qf)[KS], float& m_run, float& l_run,
-                                                   f32x4 (&oacc)[MB]) {
+    template <bool VAR>
+    static __device__ __forceinline__ void compute(const uint16_t* stage, int lane, int t0, int lo, int limit,
+                                                   float sl2, float cap_l2, float cap_inv2, const u32x4 (&qf)[KS],
+                                                   float& m_run, float& l_run, f32x4 (&oacc)[MB]) {
         const uint16_t* const kl = stage;
         const uint16_t* const vl = stage + K_ELEMS;
         const int row = lane & 15;
@@ -190,7 +242,13 @@ struct DecodeTile {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = t0 + b * 16 + G * 4 + i;
-                const float x = key < limit ? sacc[b][i] * sl2 : -INFINITY;
+                float x = sacc[b][i] * sl2;
+                if constexpr (VAR) {
+                    if (cap_l2 > 0.f) x = softcap_l2(x, cap_l2, cap_inv2);
+                    x = key < limit && key >= lo ? x : -INFINITY;
+                } else {
+                    x = key < limit ? x : -INFINITY;
+                }
                 sv[b * 4 + i] = x;
                 mx = fmaxf(mx, x);
             }
@@ -240,6 +298,13 @@ __device__ __forceinline__ void load_decode_q(const FwdParams& p, int lane, int 
     for (int ks = 0; ks < HD / 32; ++ks) qf[ks] = row_ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
 }
 
+// First key query row (lane % 16) of an item may see (the sliding window).
+__device__ __forceinline__ int decode_row_lo(const FwdParams& p, int lane, int q_len, int L) {
+    const int row = lane & 15;
+    if (row >= q_len * p.g) return 0;
+    return window_lo(p, L - q_len + row / p.g);
+}
+
 // Largest key index + 1 that query row (lane % 16) of an item may see.
 __device__ __forceinline__ int decode_row_limit(const FwdParams& p, int lane, int q_len, int L) {
     const int row = lane & 15;
@@ -254,7 +319,7 @@ __device__ __forceinline__ int decode_row_limit(const FwdParams& p, int lane, in
 // `stage` is the wave's LDS area. Returns the wave's online-softmax state: m
 // (log2 domain, row-uniform), l (summed over the row), and O^T (lane holds
 // row l%16, head-dim elements 16*mb + 4*(l/16) + i).
-template <int HD, bool FP8, bool PAGED>
+template <int HD, bool FP8, bool PAGED, bool VAR>
 __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage, int lane, int r, int kh, int q0,
                                              int q_len, int L, int k_first, int step, int k_end, float& m_run,
                                              float& l_run, f32x4 (&oacc)[HD / 16]) {
@@ -263,6 +328,7 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage
     u32x4 qf[DT::KS];
     load_decode_q<HD>(p, lane, q0, q_len * p.g, kh, qf);
     const int limit = min(decode_row_limit(p, lane, q_len, L), k_end);
+    const int lo = VAR ? decode_row_lo(p, lane, q_len, L) : 0;
     float sl2 = p.scale_log2;
     if constexpr (FP8) sl2 *= *p.k_scale;
     const int32_t* bt_row = PAGED ? p.bt + (int64_t)r * p.bt_stride : nullptr;
@@ -318,7 +384,8 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage
             page_for(t_cur + 2 * step, pg);
             DT::load(p, lane, rows, kh, kr, vr);
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
-            DT::compute(stage, lane, t_cur, limit, sl2, qf, m_run, l_run, oacc);
+            DT::template compute<VAR>(stage, lane, t_cur, lo, limit, sl2, p.softcap_l2, p.softcap_inv2, qf, m_run,
+                                      l_run, oacc);
             row_from(t_cur + 2 * step, pg, rows);
             t_cur += step;
             if (t_cur >= k_end) break;
@@ -333,7 +400,9 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage
 
 // Split-KV decode: one workgroup per (KV split, kv head, request); its four
 // waves take interleaved tiles of the split and merge their states in LDS.
-template <int HD, bool FP8, bool PAGED>
+// VAR: the sliding window / soft cap code is compiled in (sinks cost
+// nothing when absent and are always handled).
+template <int HD, bool FP8, bool PAGED, bool VAR>
 __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParams p) {
     constexpr int TILE = kDecodeTile;
     constexpr int NW = kDecodeWaves;
@@ -350,13 +419,14 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
     const int q_len = p.qsl[r + 1] - q0;
     if (q_len <= 0) return;
     const int L = p.seq_lens ? p.seq_lens[r] : q_len;
-    const int k_begin = p.num_splits > 1 ? s * p.split_len : 0;
+    const int base = VAR ? window_base(p, q_len, L) : 0;
+    const int k_begin = base + (p.num_splits > 1 ? s * p.split_len : 0);
     const int k_end = p.num_splits > 1 ? min(L, k_begin + p.split_len) : L;
     if (k_begin >= k_end) return;  // no row of this item sees a key here; the merge never reads it
 
     float m_run, l_run;
     f32x4 oacc[MB];
-    decode_range<HD, FP8, PAGED>(p, smem + w * DecodeTile<HD, FP8>::ELEMS, lane, r, kh, q0, q_len, L, k_begin + w * TILE,
+    decode_range<HD, FP8, PAGED, VAR>(p, smem + w * DecodeTile<HD, FP8>::ELEMS, lane, r, kh, q0, q_len, L, k_begin + w * TILE,
                                  NW * TILE,
                                  k_end, m_run, l_run, oacc);
     const int row = lane & 15;
@@ -380,6 +450,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
     const int fc = (threadIdx.x & 15) * PER;
     if (frow >= rows_total) return;
     const float vsc = FP8 ? *p.v_scale : 1.f;
+    const int64_t tok = q0 + frow / g;
+    const int head = kh * g + frow % g;
     float M = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i][frow]);
@@ -390,7 +462,10 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
         wt[i] = fast_exp2(sm_m[i][frow] - Mu);
         Lt += wt[i] * sm_l[i][frow];
     }
-    const float inv = Lt > 0.f ? vsc / Lt : 0.f;
+    // the sink joins the normaliser once, in the final output (split
+    // partials leave it to the merge)
+    float inv, lse;
+    finalize_row(M, Lt, p.num_splits == 1 ? sink_l2(p, head) : -INFINITY, vsc, inv, lse);
     float o[PER];
 #pragma unroll
     for (int d = 0; d < PER; ++d) {
@@ -399,9 +474,6 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
         for (int i = 0; i < NW; ++i) a += wt[i] * co[(i * 16 + frow) * HD + fc + d];
         o[d] = a * inv;
     }
-    const float lse = Lt > 0.f ? (Mu + fast_log2(Lt)) * kLn2 : -INFINITY;
-    const int64_t tok = q0 + frow / g;
-    const int head = kh * g + frow % g;
     if (p.num_splits == 1) {
         store_bf16<PER>((uint16_t*)p.out + (tok * p.H + head) * HD + fc, o);
         if (p.lse && (threadIdx.x & 15) == 0) p.lse[(int64_t)head * p.T + tok] = lse;
@@ -423,27 +495,39 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
 // for each row, the partials of the waves wave_of(first tile of its item) ..
 // wave_of(last tile), which are exactly the waves that wrote them.
 
-__device__ __forceinline__ int decode_tiles_of(const FwdParams& p, int r) {
+// Tiles of one item of request r: from the window base (0 without a
+// window) to the last key.
+// (VAR false: no window, known at compile time.)
+template <bool VAR = true>
+__device__ __forceinline__ int decode_first_tile(const FwdParams& p, int q_len, int L) {
+    return VAR ? window_base(p, q_len, L) / kDecodeTile : 0;
+}
+template <bool VAR = true>
+__device__ __forceinline__ int decode_tiles_of(const FwdParams& p, int q_len, int L) {
+    return q_len <= 0 ? 0 : (L + kDecodeTile - 1) / kDecodeTile - decode_first_tile<VAR>(p, q_len, L);
+}
+template <bool VAR>
+__device__ __forceinline__ int decode_tiles_of_request(const FwdParams& p, int r) {
     const int ql = p.qsl[r + 1] - p.qsl[r];
-    if (ql <= 0) return 0;
-    const int L = p.seq_lens ? p.seq_lens[r] : ql;
-    return (L + kDecodeTile - 1) / kDecodeTile;
+    return decode_tiles_of<VAR>(p, ql, p.seq_lens ? p.seq_lens[r] : ql);
 }
 
 // Wave index whose tile range holds global tile t (ranges [w N / W, (w+1) N / W)).
 __device__ __forceinline__ int64_t wave_of_tile(int64_t t, int64_t N, int64_t W) { return ((t + 1) * W - 1) / N; }
 
 // Position of a decode wave in the global tile list: request r, kv head kh,
-// tile t of the (r, kh) item, global index T, with request r's tiles per
-// item (n), KV length (L) and query range (q0, q_len). An invalid cursor
-// (past the wave's range) keeps pointing at the wave's last tile.
+// tile t of the (r, kh) item (key tile t0 + t of the request), global index
+// T, with request r's tiles per item (n), first tile (t0), KV length (L) and
+// query range (q0, q_len). An invalid cursor (past the wave's range) keeps
+// pointing at the wave's last tile.
 struct DecodeCursor {
     int64_t T;
-    int r, kh, t, n, L, q0, q_len;
+    int r, kh, t, n, t0, L, q0, q_len;
     bool valid;
+    __device__ __forceinline__ int key0() const { return (t0 + t) * kDecodeTile; }
 };
 
-template <int HD, bool FP8, bool PAGED>
+template <int HD, bool FP8, bool PAGED, bool VAR>
 __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel(FwdParams p) {
     using DT = DecodeTile<HD, FP8>;
     constexpr int TILE = kDecodeTile;
@@ -459,7 +543,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     // also publishes the per-request tile prefix for the merge kernel
     int total = 0;
     for (int base = 0; base < p.B; base += 64) {
-        int n = base + lane < p.B ? decode_tiles_of(p, base + lane) : 0;
+        int n = base + lane < p.B ? decode_tiles_of_request<VAR>(p, base + lane) : 0;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
         total += __builtin_amdgcn_readfirstlane(n);
@@ -471,7 +555,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     int r = -1, pr = 0, carry = 0;
     for (int base = 0; base < p.B; base += 64) {
         const int rr = base + lane;
-        const int n = rr < p.B ? decode_tiles_of(p, rr) : 0;
+        const int n = rr < p.B ? decode_tiles_of_request<VAR>(p, rr) : 0;
         int incl = n;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -493,7 +577,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     if (T0 >= T1 || r < 0) return;
 
     // Request metadata window: lane j describes request wb + j.
-    int wb = -1, w_n = 0, w_L = 0, w_q0 = 0, w_ql = 0;
+    int wb = -1, w_n = 0, w_t0 = 0, w_L = 0, w_q0 = 0, w_ql = 0;
     auto fill = [&](DecodeCursor& c) {
         if (wb < 0 || c.r >= wb + 64) {
             wb = c.r;
@@ -501,10 +585,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
             w_q0 = x < p.B ? p.qsl[x] : 0;
             w_ql = x < p.B ? p.qsl[x + 1] - w_q0 : 0;
             w_L = x < p.B ? (p.seq_lens ? p.seq_lens[x] : w_ql) : 0;
-            w_n = w_ql > 0 ? (w_L + TILE - 1) / TILE : 0;
+            w_n = decode_tiles_of<VAR>(p, w_ql, w_L);
+            if constexpr (VAR) w_t0 = decode_first_tile<VAR>(p, w_ql, w_L);
         }
         const int j = __builtin_amdgcn_readfirstlane(c.r - wb);
         c.n = __builtin_amdgcn_readlane(w_n, j);
+        if constexpr (VAR) c.t0 = __builtin_amdgcn_readlane(w_t0, j);
+        else c.t0 = 0;
         c.L = __builtin_amdgcn_readlane(w_L, j);
         c.q0 = __builtin_amdgcn_readlane(w_q0, j);
         c.q_len = __builtin_amdgcn_readlane(w_ql, j);
@@ -555,7 +642,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     auto page_for = [&](const DecodeCursor& c, int (&pg)[NL]) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int pos = min(c.t * TILE + DT::key_of(lane, i), c.L - 1);
+            const int pos = min(c.key0() + DT::key_of(lane, i), c.L - 1);
             if constexpr (PAGED) pg[i] = p.bt[(int64_t)c.r * p.bt_stride + page_index(pos, p.bs, p.bs_shift)];
             else pg[i] = c.q0 + pos;
         }
@@ -563,7 +650,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     auto row_from = [&](const DecodeCursor& c, const int (&pg)[NL], int (&rows)[NL]) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int pos = min(c.t * TILE + DT::key_of(lane, i), c.L - 1);
+            const int pos = min(c.key0() + DT::key_of(lane, i), c.L - 1);
             if constexpr (PAGED) rows[i] = pg[i] * p.bs + page_offset(pos, p.bs, p.bs_shift);
             else rows[i] = pg[i];
         }
@@ -579,6 +666,11 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     u32x4 qf[DT::KS], qn[DT::KS];
     load_decode_q<HD>(p, lane, c0.q0, c0.q_len * p.g, c0.kh, qf);
     int limit = decode_row_limit(p, lane, c0.q_len, c0.L);
+    int lo = VAR ? decode_row_lo(p, lane, c0.q_len, c0.L) : 0;
+    // sink logit of this lane's row (log2 domain), loaded with the item's
+    // query fragment
+    const bool has_sinks = p.sinks != nullptr;
+    float sk = has_sinks ? sink_l2(p, c0.kh * p.g + row % p.g) : -INFINITY, sk_next = -INFINITY;
     int seg_t0 = c0.t;  // first tile of the current item segment
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 oacc[MB];
@@ -601,12 +693,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
         float l = l_run;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        const float inv = l > 0.f ? vsc / l : 0.f;
-        const float mu = m_run == -INFINITY ? 0.f : m_run;
-        w_lse = l > 0.f ? (mu + fast_log2(l)) * kLn2 : -INFINITY;
+        w_whole = seg_t0 == 0 && c.t == c.n - 1;
+        // a sink joins the normaliser once: in the final output of a whole
+        // item, else in the merge
+        float inv;
+        finalize_row(m_run, l, w_whole ? sk : -INFINITY, vsc, inv, w_lse);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) oacc[mb] *= inv;
-        w_whole = seg_t0 == 0 && c.t == c.n - 1;
         wc = c;
     };
     auto write = [&]() {
@@ -658,9 +751,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
         page_for(c2, pg);
         DT::load(p, lane, rows, c1.kh, kr, vr);
         const bool c1_new = c1.valid && c1.t == 0;
-        if (c1_new) load_decode_q<HD>(p, lane, c1.q0, c1.q_len * p.g, c1.kh, qn);
+        if (c1_new) {
+            load_decode_q<HD>(p, lane, c1.q0, c1.q_len * p.g, c1.kh, qn);
+            if (has_sinks) sk_next = sink_l2(p, c1.kh * p.g + row % p.g);
+        }
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
-        DT::compute(stage, lane, c0.t * TILE, limit, sl2, qf, m_run, l_run, oacc);
+        DT::template compute<VAR>(stage, lane, c0.key0(), lo, limit, sl2, p.softcap_l2, p.softcap_inv2, qf, m_run,
+                                  l_run, oacc);
         if (!c1.valid || c1_new) {
             close(c0);
             pending = true;
@@ -674,6 +771,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
 #pragma unroll
             for (int ks = 0; ks < DT::KS; ++ks) qf[ks] = qn[ks];
             limit = decode_row_limit(p, lane, c0.q_len, c0.L);
+            if constexpr (VAR) lo = decode_row_lo(p, lane, c0.q_len, c0.L);
+            sk = sk_next;
             seg_t0 = 0;
         }
         DT::store(stage, lane, kr, vr);
@@ -762,7 +861,8 @@ constexpr int kTileRows = 64;
 //  kPgFlat: no block table; K/V rows are packed like q.
 constexpr int kPgAny = 0, kPgWide = 1, kPgFlat = 2;
 
-template <int HD, bool FP8, int PG>
+// VAR: the sliding window / soft cap code is compiled in.
+template <int HD, bool FP8, int PG, bool VAR>
 __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdParams p) {
     constexpr int NW = kPrefillWaves;           // waves per workgroup
     constexpr int ROWS = prefill_rows(HD);      // query rows per work item
@@ -813,8 +913,11 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     const int ctx = L - q_len;
     const int tok_last = min(q_len, tok0 + tpw) - 1;
     const int item_end = p.causal ? min(L, ctx + tok_last + 1) : L;
-    const int k_begin = p.num_splits > 1 ? s * p.split_len : 0;
-    const int k_end = p.num_splits > 1 ? min(item_end, k_begin + p.split_len) : item_end;
+    // with a sliding window no row of the item sees a key below the window
+    // of its first token (a split that lies wholly below it is never read)
+    const int k_split = (VAR ? window_base(p, q_len, L) : 0) + (p.num_splits > 1 ? s * p.split_len : 0);
+    const int k_begin = VAR ? max(k_split, window_lo(p, ctx + tok0) & ~(TILE - 1)) : k_split;
+    const int k_end = p.num_splits > 1 ? min(item_end, k_split + p.split_len) : item_end;
     if (k_begin >= k_end) return;
 
     // this lane's query row
@@ -825,12 +928,20 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     const int head = kh * g + rho % g;
     int limit = p.causal ? min(L, ctx + tl + 1) : L;
     limit = row_ok ? min(limit, k_end) : 0;
+    const int lo = VAR ? window_lo(p, ctx + tl) : 0;  // first key the row sees
     // keys below wave_min are visible to every valid row of the wave: tiles
     // that end there need no mask (rows past the end of the request are never
     // stored, so their scores do not matter)
     const int wtok_first = tok0 + (w * kPrefillRowsPerWave) / g;
     const bool wave_any = wtok_first < q_len && w * kPrefillRowsPerWave < tpw * g;
     const int wave_min = !wave_any ? k_begin : (p.causal ? min(k_end, ctx + wtok_first + 1) : k_end);
+    // with a sliding window, keys at or past wave_lo are visible to every
+    // valid row of the wave: tiles that start there need no lower mask
+    int wave_lo = 0;
+    if (VAR && wave_any) {
+        const int wrho_last = min(w * kPrefillRowsPerWave + kPrefillRowsPerWave, tpw * g) - 1;
+        wave_lo = window_lo(p, ctx + min(q_len - 1, tok0 + wrho_last / g));
+    }
 
     u32x4 qf[KS];
     {
@@ -843,6 +954,11 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         sl2 *= *p.k_scale;
         vsc = *p.v_scale;
     }
+    // With the soft cap the scores are scaled and capped in place (log2
+    // domain) before the mask, and the softmax then takes them with scale 1.
+    const bool capped = VAR && p.softcap_l2 > 0.f;
+    const float sl2_cap = sl2;
+    if (capped) sl2 = 1.f;
 
     // Per-lane LDS read offsets. The chunk permutation only touches the bits
     // in SWMASK and depends on row bits 0..3, so the other chunk bits, the
@@ -967,15 +1083,28 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
                     qf[ks], sacc[kb]);
         }
     };
-    // causal / length mask of a tile that reaches past wave_min
-    auto mask = [&](int t0, f32x16 (&sacc)[KB]) {
-        if (t0 + TILE > wave_min) {
-            const int lim = limit - t0 - hsel * 4;
+    // soft cap of a tile's scores (before the mask)
+    auto cap = [&](f32x16 (&sacc)[KB]) {
+        if (capped) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (kb * 32 + (e >> 2) * 8 + (e & 3) >= lim) sacc[kb][e] = -INFINITY;
+                for (int e = 0; e < 16; ++e) sacc[kb][e] = softcap_l2(sacc[kb][e] * sl2_cap, p.softcap_l2, p.softcap_inv2);
+        }
+    };
+    // causal / length mask of a tile that reaches past wave_min, window mask
+    // of one that starts below wave_lo
+    auto mask = [&](int t0, f32x16 (&sacc)[KB]) {
+        if (t0 + TILE > wave_min || (VAR && t0 < wave_lo)) {
+            const int lim = limit - t0 - hsel * 4;
+            const int low = lo - t0 - hsel * 4;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int k = kb * 32 + (e >> 2) * 8 + (e & 3);
+                    if (k >= lim || (VAR && k < low)) sacc[kb][e] = -INFINITY;
+                }
         }
     };
     // row maximum of a tile (both lane halves hold keys of the same row)
@@ -1062,6 +1191,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         qk(k_lds0, s_a);
+        cap(s_a);
         mask(k_begin, s_a);
         mx = rowmax(s_a);
         __syncthreads();
@@ -1087,7 +1217,10 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         u32x4 pf[2 * KB];
         if constexpr (!LAST) qk(k_next, sn);
         expo(sc, pf);
-        if constexpr (!LAST) mask(t0 + TILE, sn);
+        if constexpr (!LAST) {
+            cap(sn);
+            mask(t0 + TILE, sn);
+        }
         pv(v_here, pf);
         if constexpr (!LAST) {
             mx = rowmax(sn);
@@ -1117,9 +1250,9 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
 
     if (!row_ok) return;
     l_run += __shfl_xor(l_run, 32);
-    const float inv = l_run > 0.f ? vsc / l_run : 0.f;
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    const float lse = l_run > 0.f ? (m_use + fast_log2(l_run)) * kLn2 : -INFINITY;
+    // a sink joins the normaliser once, in the final output
+    float inv, lse;
+    finalize_row(m_run, l_run, p.num_splits == 1 ? sink_l2(p, head) : -INFINITY, vsc, inv, lse);
     const int64_t tok = q0 + tl;
     if (p.num_splits == 1) {
         uint16_t* op = (uint16_t*)p.out + (tok * p.H + head) * HD + hsel * 4;
@@ -1165,9 +1298,10 @@ __global__ __launch_bounds__(64) void generic_kernel(FwdParams p) {
     const int t = (int)(tok - q0);
     const int L = p.seq_lens ? p.seq_lens[r] : q_len;
     const int n_vis = p.causal ? max(0, min(L, L - q_len + t + 1)) : L;
-    const int k_begin = p.num_splits > 1 ? s * p.split_len : 0;
-    const int k_end = p.num_splits > 1 ? min(n_vis, k_begin + p.split_len) : n_vis;
-    if (p.num_splits > 1 && k_begin >= n_vis) return;
+    const int k_split = window_base(p, q_len, L) + (p.num_splits > 1 ? s * p.split_len : 0);
+    const int k_end = p.num_splits > 1 ? min(n_vis, k_split + p.split_len) : n_vis;
+    if (p.num_splits > 1 && k_split >= n_vis) return;
+    const int k_begin = max(k_split, window_lo(p, L - q_len + t));
     const int hd = p.hd;
     const int kh = h / p.g;
     float qv[4], acc[4];
@@ -1198,7 +1332,8 @@ __global__ __launch_bounds__(64) void generic_kernel(FwdParams p) {
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-        const float x = dot * sl2;
+        float x = dot * sl2;
+        if (p.softcap_l2 > 0.f) x = softcap_l2(x, p.softcap_l2, p.softcap_inv2);
         const float m_new = fmaxf(m, x);
         const float alpha = fast_exp2(m - m_new);
         const float pj = fast_exp2(x - m_new);
@@ -1210,8 +1345,8 @@ __global__ __launch_bounds__(64) void generic_kernel(FwdParams p) {
         }
         m = m_new;
     }
-    const float inv = l > 0.f ? vsc / l : 0.f;
-    const float lse = l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
+    float inv, lse;
+    finalize_row(m, l, p.num_splits == 1 ? sink_l2(p, h) : -INFINITY, vsc, inv, lse);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int d = lane + 64 * i;
@@ -1237,8 +1372,11 @@ __global__ __launch_bounds__(64) void generic_kernel(FwdParams p) {
 // ----------------------------------------------------------------- combine
 
 // Merge of the split partials. Split s of a row holds keys
-// [s * split_len, (s+1) * split_len); only splits below
-// ceil(n_vis / split_len) were written, and only those are read.
+// [base + s * split_len, base + (s+1) * split_len) (base: the request's
+// window base, 0 without a window). The splits that hold the row's visible
+// keys [lo, n_vis) are s_lo = (lo - base) / split_len up to
+// ceil((n_vis - base) / split_len) - 1; every kernel writes at least those,
+// and only those are read. A sink logit joins the normaliser here.
 // One half-wave (32 lanes) per (token, head) row: lane j first holds the lse
 // of splits j, j+32, ... and their weights, then the lanes accumulate
 // 4-element chunks of the row over all splits, with independent loads.
@@ -1257,14 +1395,17 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
     const int L = p.seq_lens ? p.seq_lens[r] : q_len;
     const int t = (int)(tok - q0);
     const int n_vis = p.causal ? max(0, min(L, L - q_len + t + 1)) : L;
-    const int n_valid = min(p.num_splits, (n_vis + p.split_len - 1) / p.split_len);
+    const int base = window_base(p, q_len, L);
+    const int s_lo = max(0, window_lo(p, L - q_len + t) - base) / p.split_len;
+    const int s_end = min(p.num_splits, max(0, n_vis - base + p.split_len - 1) / p.split_len);
+    const int n_valid = max(0, s_end - s_lo);  // splits s_lo + j, j < n_valid
     const int nc = (n_valid + 31) >> 5;
     float ls[MAXC];
     float M = -INFINITY;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-        const int sp = c * 32 + hl;
-        ls[c] = (c < nc && sp < n_valid) ? p.part_lse[((int64_t)sp * p.H + h) * p.T + tok] : -INFINITY;
+        const int sp = s_lo + c * 32 + hl;
+        ls[c] = (c < nc && c * 32 + hl < n_valid) ? p.part_lse[((int64_t)sp * p.H + h) * p.T + tok] : -INFINITY;
         M = fmaxf(M, ls[c]);
     }
 #pragma unroll
@@ -1278,8 +1419,8 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    const float lse = wsum > 0.f ? M + fast_log2(wsum) * kLn2 : -INFINITY;
+    float inv, lse;
+    finalize_row(Mu * kLog2e, wsum, sink_l2(p, h), 1.f, inv, lse);
     const int nch = p.hd / 4;  // 4-element chunks per row (<= 64)
     const int base_lane = lane & 32;
     for (int cc = hl; cc < ((nch + 31) & ~31); cc += 32) {
@@ -1288,7 +1429,7 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
             const int cnt = min(32, n_valid - c * 32);
             for (int j = 0; j < cnt; ++j) {
                 const float wgt = __shfl(ls[c], base_lane + j);
-                const int sp = c * 32 + j;
+                const int sp = s_lo + c * 32 + j;
                 if (cc < nch) o += wgt * *(const f32x4*)(p.part_o + (((int64_t)sp * p.T + tok) * p.H + h) * p.hd + 4 * cc);
             }
         }
@@ -1322,7 +1463,7 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
     const int L = p.seq_lens ? p.seq_lens[r] : q_len;
     const int64_t N = (int64_t)p.Hkv * p.sk_prefix[p.B];
     const int64_t first = (int64_t)p.Hkv * p.sk_prefix[r];
-    const int n_r = (L + kDecodeTile - 1) / kDecodeTile;
+    const int n_r = decode_tiles_of(p, q_len, L);
     const int64_t W = p.sk_waves;
     const int64_t g0 = first + (int64_t)kh * n_r;
     const int64_t wf = wave_of_tile(g0, N, W), wl = wave_of_tile(g0 + n_r - 1, N, W);
@@ -1382,7 +1523,8 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    float inv, lse;
+    finalize_row(Mu * kLog2e, wsum, sink_l2(p, h), 1.f, inv, lse);
     uint16_t* dst = (uint16_t*)p.out + (tok * p.H + h) * p.hd;
     if (c0) {
         o0 *= inv;
@@ -1392,7 +1534,7 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
         o1 *= inv;
         *(u32x2*)(dst + 4 * (hl + 32)) = u32x2{pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
     }
-    if (p.lse && hl == 0) p.lse[(int64_t)h * p.T + tok] = wsum > 0.f ? M + fast_log2(wsum) * kLn2 : -INFINITY;
+    if (p.lse && hl == 0) p.lse[(int64_t)h * p.T + tok] = lse;
 }
 
 template <bool F32>
@@ -1436,16 +1578,25 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, float* out_lse, c
 
 // ----------------------------------------------------------------- launchers
 
+// The decode kernels are built with and without the window / soft cap code.
+static bool uses_var(const FwdParams& p) { return p.window_left >= 0 || p.softcap_l2 > 0.f; }
+template <typename K1, typename K0>
+static void launch_var(K1 with_var, K0 plain, bool var, dim3 grid, hipStream_t s, const FwdParams& p) {
+    if (var) hipLaunchKernelGGL(with_var, grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(plain, grid, dim3(256), 0, s, p);
+}
+
 template <int HD>
 static hipError_t decode_hd(const FwdParams& p, KvType kv, hipStream_t s) {
     dim3 grid(p.num_splits, p.Hkv, p.B);
+    const bool var = uses_var(p);
     const bool paged = p.bt != nullptr;
     if (kv == KvType::FP8) {
-        if (paged) hipLaunchKernelGGL((decode_kernel<HD, true, true>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((decode_kernel<HD, true, false>), grid, dim3(256), 0, s, p);
+        if (paged) launch_var((decode_kernel<HD, true, true, true>), (decode_kernel<HD, true, true, false>), var, grid, s, p);
+        else launch_var((decode_kernel<HD, true, false, true>), (decode_kernel<HD, true, false, false>), var, grid, s, p);
     } else {
-        if (paged) hipLaunchKernelGGL((decode_kernel<HD, false, true>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((decode_kernel<HD, false, false>), grid, dim3(256), 0, s, p);
+        if (paged) launch_var((decode_kernel<HD, false, true, true>), (decode_kernel<HD, false, true, false>), var, grid, s, p);
+        else launch_var((decode_kernel<HD, false, false, true>), (decode_kernel<HD, false, false, false>), var, grid, s, p);
     }
     return hipGetLastError();
 }
@@ -1453,13 +1604,14 @@ static hipError_t decode_hd(const FwdParams& p, KvType kv, hipStream_t s) {
 template <int HD>
 static hipError_t decode_balanced_hd(const FwdParams& p, KvType kv, hipStream_t s) {
     dim3 grid(p.sk_waves / 4);
+    const bool var = uses_var(p);
     const bool paged = p.bt != nullptr;
     if (kv == KvType::FP8) {
-        if (paged) hipLaunchKernelGGL((decode_balanced_kernel<HD, true, true>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((decode_balanced_kernel<HD, true, false>), grid, dim3(256), 0, s, p);
+        if (paged) launch_var((decode_balanced_kernel<HD, true, true, true>), (decode_balanced_kernel<HD, true, true, false>), var, grid, s, p);
+        else launch_var((decode_balanced_kernel<HD, true, false, true>), (decode_balanced_kernel<HD, true, false, false>), var, grid, s, p);
     } else {
-        if (paged) hipLaunchKernelGGL((decode_balanced_kernel<HD, false, true>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((decode_balanced_kernel<HD, false, false>), grid, dim3(256), 0, s, p);
+        if (paged) launch_var((decode_balanced_kernel<HD, false, true, true>), (decode_balanced_kernel<HD, false, true, false>), var, grid, s, p);
+        else launch_var((decode_balanced_kernel<HD, false, false, true>), (decode_balanced_kernel<HD, false, false, false>), var, grid, s, p);
     }
     return hipGetLastError();
 }
@@ -1494,14 +1646,15 @@ static hipError_t prefill_hd(const FwdParams& p, KvType kv, hipStream_t s) {
     dim3 grid((unsigned)(streams_per_xcd * kXcds * p.n_qtiles), p.num_splits);
     const dim3 block(64 * kPrefillWaves);
     const int pg = !p.bt ? kPgFlat : (p.bs_shift >= 4 ? kPgWide : kPgAny);
+    const bool var = uses_var(p);
     if (kv == KvType::FP8) {
-        if (pg == kPgFlat) hipLaunchKernelGGL((prefill_kernel<HD, true, kPgFlat>), grid, block, 0, s, p);
-        else if (pg == kPgWide) hipLaunchKernelGGL((prefill_kernel<HD, true, kPgWide>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((prefill_kernel<HD, true, kPgAny>), grid, block, 0, s, p);
+        if (pg == kPgFlat) launch_var((prefill_kernel<HD, true, kPgFlat, true>), (prefill_kernel<HD, true, kPgFlat, false>), var, grid, s, p);
+        else if (pg == kPgWide) launch_var((prefill_kernel<HD, true, kPgWide, true>), (prefill_kernel<HD, true, kPgWide, false>), var, grid, s, p);
+        else launch_var((prefill_kernel<HD, true, kPgAny, true>), (prefill_kernel<HD, true, kPgAny, false>), var, grid, s, p);
     } else {
-        if (pg == kPgFlat) hipLaunchKernelGGL((prefill_kernel<HD, false, kPgFlat>), grid, block, 0, s, p);
-        else if (pg == kPgWide) hipLaunchKernelGGL((prefill_kernel<HD, false, kPgWide>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((prefill_kernel<HD, false, kPgAny>), grid, block, 0, s, p);
+        if (pg == kPgFlat) launch_var((prefill_kernel<HD, false, kPgFlat, true>), (prefill_kernel<HD, false, kPgFlat, false>), var, grid, s, p);
+        else if (pg == kPgWide) launch_var((prefill_kernel<HD, false, kPgWide, true>), (prefill_kernel<HD, false, kPgWide, false>), var, grid, s, p);
+        else launch_var((prefill_kernel<HD, false, kPgAny, true>), (prefill_kernel<HD, false, kPgAny, false>), var, grid, s, p);
     }
     return hipGetLastError();
 }

@@ -31,6 +31,11 @@ struct FwdParams {
     // balanced decode schedule
     int32_t sk_waves;         // waves sharing the decode tiles (grid = sk_waves / 4 workgroups)
     int32_t* sk_prefix;       // [B+1] per-request tile prefix and total, written by the attention kernel
+    // attention variants
+    int32_t window_left;      // < 0: no sliding window
+    float softcap_l2;         // softcap * log2(e) (> 0), or 0: no soft cap
+    float softcap_inv2;       // 2 / softcap (soft cap on)
+    const float* sinks;       // [H] natural-log sink logits, or nullptr
 };
 
 enum class KvType { BF16, FP8, F32 };

@@ -85,6 +85,10 @@ def test_valid_args_pass():
     (dict(num_splits=-1), pkv.PKV_ERR_INVALID_ARG),
     (dict(num_splits=300), pkv.PKV_ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
+    (dict(sliding_window=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(softcap=-1.0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(softcap=float("inf")), pkv.PKV_ERR_INVALID_ARG),
+    (dict(softcap=float("nan")), pkv.PKV_ERR_INVALID_ARG),
     (dict(num_tokens=-1), pkv.PKV_ERR_INVALID_ARG),
 ])
 def test_invalid_args_rejected(kw, status):
@@ -120,6 +124,24 @@ def test_split_plan_and_workspace():
     s = L.pkv_varlen_num_splits(ctypes.byref(b))
     assert 2 <= s <= 64
     assert L.pkv_varlen_workspace_size(ctypes.byref(b)) == s * 256 * 8 * (128 + 1) * 4
+
+
+def test_window_limits_the_split_span():
+    # a prefill of 256 new tokens on a 65280-token context, one request, 16
+    # work items: without a window it is split into 32 key ranges; with a
+    # 1024-key window a query sees keys from its request's window base on, a
+    # span of at most 1023 + 256 + 63 = 1342 keys, so ceil(1342 / 512) = 3
+    # splits of at least 512 keys, and a forced 64 becomes ceil(1342 / 256) = 6
+    # (split lengths are multiples of 256 keys)
+    L = pkv.lib()
+    b = good_args(num_tokens=256, num_seqs=1, num_heads=8, num_kv_heads=8, max_seqlen_q=256, max_seqlen_k=65536,
+                  block_size=16, block_table_stride=4096, num_blocks=5000)
+    assert L.pkv_varlen_num_splits(ctypes.byref(b)) == 32
+    b.sliding_window = 1024
+    assert L.pkv_varlen_num_splits(ctypes.byref(b)) == 3
+    assert L.pkv_varlen_workspace_size(ctypes.byref(b)) == 3 * 256 * 8 * (128 + 1) * 4
+    b.num_splits = 64
+    assert L.pkv_varlen_num_splits(ctypes.byref(b)) == 6
 
 
 def test_forced_split_without_workspace_is_an_error():
