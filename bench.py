@@ -13,7 +13,8 @@ heads, head size 128, bf16), batch 64, one query token per request, context
 lengths uniform in [512, 4096], page size 16, random block table. The metric is
 KV bytes read per second (GB/s) against the MI355X HBM peak of 8 TB/s.
 Other workloads (--workload): chunked_prefill (TFLOP/s against the 2.5 PFLOP/s
-bf16 dense MFMA peak), long_decode, long_decode_cascade, fp8_decode. The
+bf16 dense MFMA peak), long_decode, long_decode_cascade, fp8_decode,
+spec_decode (several new tokens per request; KV GB/s). The
 attention variants can be switched on for any workload but the cascade
 (--sliding-window W, --softcap C, --sinks); bytes and flops then count only
 what the window leaves visible.
@@ -45,7 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
 KERNEL_SOURCES = ["pkv_attn.hip", "pkv_device.h", "pkv_kernels.h"]
 DOMINANT_KERNEL = {"paged_decode": "decode_balanced_kernel", "chunked_prefill": "prefill_kernel",
                    "long_decode": "decode_balanced_kernel", "long_decode_cascade": "decode_balanced_kernel",
-                   "fp8_decode": "decode_balanced_kernel"}
+                   "fp8_decode": "decode_balanced_kernel", "spec_decode": "prefill_kernel"}
 
 WORKLOADS = {
     "paged_decode": "paged decode, 32/8 heads GQA, head 128, bf16, batch 64, ctx U[512,4096], page 16",
@@ -55,6 +56,8 @@ WORKLOADS = {
     "long_decode_cascade": "long decode as cascade: 4 requests share a 32768-token prefix, ctx 131072, "
                            "64/8 heads, head 128, bf16, page 256",
     "fp8_decode": "decode over an fp8 e4m3fn cache, bf16 q, batch 128, ctx U[1024,8192], 32/8 heads, head 128",
+    "spec_decode": "multi-token decode (speculative verification), batch 64, q_len U[2,16] on ctx U[512,4096], "
+                   "32/8 heads, head 128, bf16, page 16",
 }
 
 
@@ -74,6 +77,8 @@ def make(name, bs, over=None):
         return workloads.long_decode(shared_prefix=32768)
     if name == "fp8_decode":
         return workloads.fp8_decode(bs=bs or 16)
+    if name == "spec_decode":
+        return workloads.spec_decode(bs=bs or 16)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -307,7 +312,7 @@ def main():
     calls, main_ms, merge_ms = pkv.timing_collect()
     pkv.timing_enable(False)
 
-    use_graph = not args.eager and not cascade
+    use_graph = not args.eager
     if use_graph:
         # The K timed steps captured into one HIP graph, as a serving engine
         # captures its decode step: one untimed replay, then the timed replay.

@@ -271,8 +271,9 @@ def cascade_attention(q, k_cache, v_cache, query_start_loc, seq_lens, block_tabl
         raise ValueError("common_prefix_len must be a multiple of the block size")
     dev = q.device
     nblk = common_prefix_len // bs
-    prefix_qsl = torch.tensor([0, T], dtype=torch.int32, device=dev)
-    prefix_len = torch.tensor([common_prefix_len], dtype=torch.int32, device=dev)
+    # built on the device (no host copies), so the whole cascade can be captured in a HIP graph
+    prefix_qsl = torch.arange(2, dtype=torch.int32, device=dev) * T
+    prefix_len = torch.full((1,), common_prefix_len, dtype=torch.int32, device=dev)
     o_p, l_p = pkv_varlen_fwd(q, k_cache, v_cache, prefix_qsl, prefix_len, block_table[:1], T, common_prefix_len,
                               softmax_scale, causal=False, k_scale=k_scale, v_scale=v_scale, return_lse=True,
                               stream=stream, softcap=softcap)

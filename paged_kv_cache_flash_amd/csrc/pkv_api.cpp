@@ -48,8 +48,18 @@ struct Plan {
     int32_t splits;
     int32_t split_len;
     int32_t n_qtiles;
+    int32_t dec_rows;  // balanced decode: query rows per item slot
     size_t workspace;  // bytes needed for `splits`
 };
+
+// Query rows per balanced-decode item slot (16-row blocks) for items of
+// `rows` rows, or 0 when the balanced kernel does not take them: up to 32
+// rows over a paged cache with head size up to 128, else up to 16.
+int32_t decode_rows(const pkv_varlen_args* a, int64_t rows) {
+    if (rows <= kDecodeRows) return kDecodeRows;
+    if (a->block_table == nullptr || a->head_size > kDecodeMaxRbHead || rows > kDecodeMaxRows) return 0;
+    return 2 * kDecodeRows;
+}
 
 bool mfma_head(int hd) { return hd == 64 || hd == 128 || hd == 256; }
 
@@ -109,12 +119,16 @@ pkv_status validate_sizes(const pkv_varlen_args* a) {
 
 // Waves of the balanced decode grid: one workgroup per CU for bf16 caches;
 // fp8 tiles carry half the bytes, so two workgroups per CU keep as many bytes
-// in flight (where their LDS fits: head size up to 128).
-static int64_t balanced_waves(const pkv_varlen_args* a) {
-    return a->kv_dtype == PKV_FP8_E4M3FN && a->head_size <= 128 ? 2 * kBalancedWaves : kBalancedWaves;
+// in flight (where their LDS and registers fit: head size up to 128, items of
+// one 16-row block).
+static int64_t balanced_waves(const pkv_varlen_args* a, int32_t dec_rows) {
+    return a->kv_dtype == PKV_FP8_E4M3FN && a->head_size <= 128 && dec_rows == kDecodeRows ? 2 * kBalancedWaves
+                                                                                           : kBalancedWaves;
 }
 
-Plan make_plan(const pkv_varlen_args* a) {
+// balanced_ok false: plan without the balanced decode schedule (no room for
+// its partials).
+Plan make_plan(const pkv_varlen_args* a, bool balanced_ok = true) {
     Plan pl{};
     const int g = a->num_heads / a->num_kv_heads;
     const bool paged = a->block_table != nullptr;
@@ -127,14 +141,15 @@ Plan make_plan(const pkv_varlen_args* a) {
     const bool mfma = a->q_dtype == PKV_BF16 && mfma_head(a->head_size) && g <= kPrefillMaxGroup;
     int64_t items;
     int align;
-    if (mfma && (int64_t)a->max_seqlen_q * g <= kDecodeRows && a->num_splits == 0 &&
-        a->num_seqs <= kBalancedMaxSeqs) {
+    const int32_t drows = decode_rows(a, (int64_t)a->max_seqlen_q * g);
+    if (balanced_ok && mfma && drows > 0 && a->num_splits == 0 && a->num_seqs <= kBalancedMaxSeqs) {
         // balanced decode: balanced_waves() waves share the KV tiles equally
         pl.kind = Kind::DecodeBalanced;
-        pl.splits = (int32_t)balanced_waves(a);
+        pl.dec_rows = drows;
+        pl.splits = (int32_t)balanced_waves(a, drows);
         pl.split_len = kDecodeTile;
-        const int64_t slots = balanced_waves(a) + (int64_t)a->num_seqs * a->num_kv_heads;
-        pl.workspace = (size_t)slots * kDecodeRows * (a->head_size + 1) * sizeof(float) +
+        const int64_t slots = pl.splits + (int64_t)a->num_seqs * a->num_kv_heads;
+        pl.workspace = (size_t)slots * drows * (a->head_size + 1) * sizeof(float) +
                        (size_t)(a->num_seqs + 1) * sizeof(int32_t);
         return pl;
     }
@@ -215,11 +230,9 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     if (st != PKV_OK || a->num_tokens == 0) return st;
     Plan pl = make_plan(a);
     if (pl.kind == Kind::DecodeBalanced && (a->workspace == nullptr || a->workspace_bytes < pl.workspace)) {
-        // no room for the balanced schedule's partials: unsplit decode
-        pl.kind = Kind::Decode;
-        pl.splits = 1;
-        pl.split_len = (int32_t)std::max<int64_t>(a->block_table ? a->max_seqlen_k : a->max_seqlen_q, 1);
-        pl.workspace = 0;
+        // no room for the balanced schedule's partials: the other kernels,
+        // unsplit unless their partials fit
+        pl = make_plan(a, false);
     }
     if (pl.kind != Kind::DecodeBalanced && pl.splits > 1 &&
         (a->workspace == nullptr || a->workspace_bytes < pl.workspace)) {
@@ -264,11 +277,12 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     p.softcap_inv2 = a->softcap > 0.f ? 2.f / a->softcap : 0.f;
     p.sinks = a->sinks;
     if (pl.kind == Kind::DecodeBalanced) {
-        const int64_t slots = balanced_waves(a) + (int64_t)a->num_seqs * a->num_kv_heads;
-        p.sk_waves = (int32_t)balanced_waves(a);
+        const int64_t slots = pl.splits + (int64_t)a->num_seqs * a->num_kv_heads;
+        p.sk_waves = pl.splits;
+        p.dec_rows = pl.dec_rows;
         p.part_o = (float*)a->workspace;
-        p.part_lse = p.part_o + (size_t)slots * kDecodeRows * a->head_size;
-        p.sk_prefix = (int32_t*)(p.part_lse + (size_t)slots * kDecodeRows);
+        p.part_lse = p.part_o + (size_t)slots * pl.dec_rows * a->head_size;
+        p.sk_prefix = (int32_t*)(p.part_lse + (size_t)slots * pl.dec_rows);
     } else if (pl.splits > 1) {
         p.part_o = (float*)a->workspace;
         p.part_lse = p.part_o + (size_t)pl.splits * a->num_tokens * a->num_heads * a->head_size;

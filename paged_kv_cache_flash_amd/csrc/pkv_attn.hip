@@ -284,12 +284,13 @@ struct DecodeTile {
 // the other counters alone.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Query fragment of a decode item: lane l feeds row l % 16 (token row / g,
-// head kh * g + row % g), head-dim elements 8 * (l / 16) + 32 ks onward.
+// Query fragment of a decode item: lane l feeds row row0 + l % 16 (token
+// row / g, head kh * g + row % g), head-dim elements 8 * (l / 16) + 32 ks
+// onward.
 template <int HD>
 __device__ __forceinline__ void load_decode_q(const FwdParams& p, int lane, int q0, int rows_total, int kh,
-                                              u32x4 (&qf)[HD / 32]) {
-    const int row = lane & 15;
+                                              u32x4 (&qf)[HD / 32], int row0 = 0) {
+    const int row = row0 + (lane & 15);
     const bool row_ok = row < rows_total;
     const int tl = row_ok ? row / p.g : 0;
     const int hh = kh * p.g + (row_ok ? row % p.g : 0);
@@ -298,16 +299,16 @@ __device__ __forceinline__ void load_decode_q(const FwdParams& p, int lane, int 
     for (int ks = 0; ks < HD / 32; ++ks) qf[ks] = row_ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// First key query row (lane % 16) of an item may see (the sliding window).
-__device__ __forceinline__ int decode_row_lo(const FwdParams& p, int lane, int q_len, int L) {
-    const int row = lane & 15;
+// First key query row row0 + lane % 16 of an item may see (the sliding window).
+__device__ __forceinline__ int decode_row_lo(const FwdParams& p, int lane, int q_len, int L, int row0 = 0) {
+    const int row = row0 + (lane & 15);
     if (row >= q_len * p.g) return 0;
     return window_lo(p, L - q_len + row / p.g);
 }
 
-// Largest key index + 1 that query row (lane % 16) of an item may see.
-__device__ __forceinline__ int decode_row_limit(const FwdParams& p, int lane, int q_len, int L) {
-    const int row = lane & 15;
+// Largest key index + 1 that query row row0 + lane % 16 of an item may see.
+__device__ __forceinline__ int decode_row_limit(const FwdParams& p, int lane, int q_len, int L, int row0 = 0) {
+    const int row = row0 + (lane & 15);
     if (row >= q_len * p.g) return 0;
     return p.causal ? min(L, L - q_len + row / p.g + 1) : L;
 }
@@ -527,12 +528,17 @@ struct DecodeCursor {
     __device__ __forceinline__ int key0() const { return (t0 + t) * kDecodeTile; }
 };
 
-template <int HD, bool FP8, bool PAGED, bool VAR>
-__global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel(FwdParams p) {
+// RB: blocks of 16 query rows per item (items of up to 16 RB rows); each
+// block is a 16-column MFMA pass over the same K/V tile in LDS. With RB > 1
+// the wave holds RB running states and may use the whole register file (one
+// workgroup per CU).
+template <int HD, bool FP8, bool PAGED, bool VAR, int RB>
+__global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_balanced_kernel(FwdParams p) {
     using DT = DecodeTile<HD, FP8>;
     constexpr int TILE = kDecodeTile;
     constexpr int MB = DT::MB;
     constexpr int NL = DT::NL;
+    constexpr int ROWS = 16 * RB;
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * DT::ELEMS];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
@@ -663,19 +669,32 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     const int row = lane & 15;
     const int G = lane >> 4;
 
-    u32x4 qf[DT::KS], qn[DT::KS];
-    load_decode_q<HD>(p, lane, c0.q0, c0.q_len * p.g, c0.kh, qf);
-    int limit = decode_row_limit(p, lane, c0.q_len, c0.L);
-    int lo = VAR ? decode_row_lo(p, lane, c0.q_len, c0.L) : 0;
-    // sink logit of this lane's row (log2 domain), loaded with the item's
-    // query fragment
+    // per row block rb (rows 16 rb + lane % 16): query fragment, key bounds,
+    // sink logit (log2 domain, loaded with the item's query fragment) and
+    // running softmax state
+    // (one block prefetches the next item's query fragment with that item's
+    // first tile; several blocks load it when the item starts, to keep
+    // within the register file)
+    constexpr bool QN = RB == 1;
+    u32x4 qf[RB][DT::KS], qn[DT::KS];
+    int limit[RB], lo[RB];
+    float sk[RB], sk_next[RB], m_run[RB], l_run[RB];
+    f32x4 oacc[RB][MB];
     const bool has_sinks = p.sinks != nullptr;
-    float sk = has_sinks ? sink_l2(p, c0.kh * p.g + row % p.g) : -INFINITY, sk_next = -INFINITY;
-    int seg_t0 = c0.t;  // first tile of the current item segment
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 oacc[MB];
+    auto head_of = [&](int kh, int rb) { return kh * p.g + (16 * rb + row) % p.g; };
 #pragma unroll
-    for (int i = 0; i < MB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) {
+        load_decode_q<HD>(p, lane, c0.q0, c0.q_len * p.g, c0.kh, qf[rb], 16 * rb);
+        limit[rb] = decode_row_limit(p, lane, c0.q_len, c0.L, 16 * rb);
+        lo[rb] = VAR ? decode_row_lo(p, lane, c0.q_len, c0.L, 16 * rb) : 0;
+        sk[rb] = has_sinks ? sink_l2(p, head_of(c0.kh, rb)) : -INFINITY;
+        sk_next[rb] = -INFINITY;
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) oacc[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int seg_t0 = c0.t;  // first tile of the current item segment
 
     // The end of an item segment, in two steps. close(): normalise the
     // running output in place (oacc *= 1/l) and form its lse. write(): store
@@ -686,46 +705,53 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
     // next tile's loads covers them at no cost. (Issued after the loads, the
     // stores would have to be waited for on their own, a stall at every item
     // boundary a wave crosses.)
-    float w_lse = 0.f;
+    float w_lse[RB];
     bool w_whole = false;
     DecodeCursor wc = c0;
     auto close = [&](const DecodeCursor& c) {
-        float l = l_run;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
         w_whole = seg_t0 == 0 && c.t == c.n - 1;
-        // a sink joins the normaliser once: in the final output of a whole
-        // item, else in the merge
-        float inv;
-        finalize_row(m_run, l, w_whole ? sk : -INFINITY, vsc, inv, w_lse);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) oacc[mb] *= inv;
+        for (int rb = 0; rb < RB; ++rb) {
+            float l = l_run[rb];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            // a sink joins the normaliser once: in the final output of a
+            // whole item, else in the merge
+            float inv;
+            finalize_row(m_run[rb], l, w_whole ? sk[rb] : -INFINITY, vsc, inv, w_lse[rb]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) oacc[rb][mb] *= inv;
+        }
         wc = c;
     };
     auto write = [&]() {
-        if (row < wc.q_len * p.g) {
-            if (w_whole) {
-                const int64_t tok = wc.q0 + row / p.g;
-                const int head = wc.kh * p.g + row % p.g;
-                uint16_t* op = (uint16_t*)p.out + (tok * p.H + head) * HD + G * 4;
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    float v4[4] = {oacc[mb][0], oacc[mb][1], oacc[mb][2], oacc[mb][3]};
-                    store_bf16<4>(op + mb * 16, v4);
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r16 = 16 * rb + row;
+            if (r16 < wc.q_len * p.g) {
+                if (w_whole) {
+                    const int64_t tok = wc.q0 + r16 / p.g;
+                    const int head = head_of(wc.kh, rb);
+                    uint16_t* op = (uint16_t*)p.out + (tok * p.H + head) * HD + G * 4;
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        float v4[4] = {oacc[rb][mb][0], oacc[rb][mb][1], oacc[rb][mb][2], oacc[rb][mb][3]};
+                        store_bf16<4>(op + mb * 16, v4);
+                    }
+                    if (p.lse && G == 0) p.lse[(int64_t)head * p.T + tok] = w_lse[rb];
+                } else {
+                    const int64_t slot = gw + (int64_t)wc.r * p.Hkv + wc.kh;
+                    float* op = p.part_o + (slot * ROWS + r16) * HD + G * 4;
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) *(f32x4*)(op + mb * 16) = oacc[rb][mb];
+                    if (G == 0) p.part_lse[slot * ROWS + r16] = w_lse[rb];
                 }
-                if (p.lse && G == 0) p.lse[(int64_t)head * p.T + tok] = w_lse;
-            } else {
-                const int64_t slot = gw + (int64_t)wc.r * p.Hkv + wc.kh;
-                float* op = p.part_o + (slot * 16 + row) * HD + G * 4;
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) *(f32x4*)(op + mb * 16) = oacc[mb];
-                if (G == 0) p.part_lse[slot * 16 + row] = w_lse;
             }
-        }
-        m_run = -INFINITY;
-        l_run = 0.f;
+            m_run[rb] = -INFINITY;
+            l_run[rb] = 0.f;
 #pragma unroll
-        for (int i = 0; i < MB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < MB; ++i) oacc[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     };
 
     // One software pipeline over the wave's whole tile range, across item
@@ -751,13 +777,18 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
         page_for(c2, pg);
         DT::load(p, lane, rows, c1.kh, kr, vr);
         const bool c1_new = c1.valid && c1.t == 0;
-        if (c1_new) {
-            load_decode_q<HD>(p, lane, c1.q0, c1.q_len * p.g, c1.kh, qn);
-            if (has_sinks) sk_next = sink_l2(p, c1.kh * p.g + row % p.g);
+        if constexpr (QN) {
+            if (c1_new) {
+                load_decode_q<HD>(p, lane, c1.q0, c1.q_len * p.g, c1.kh, qn);
+                if (has_sinks) sk_next[0] = sink_l2(p, head_of(c1.kh, 0));
+            }
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
-        DT::template compute<VAR>(stage, lane, c0.key0(), lo, limit, sl2, p.softcap_l2, p.softcap_inv2, qf, m_run,
-                                  l_run, oacc);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+            if (rb == 0 || 16 * rb < c0.q_len * p.g)  // (a block without rows keeps its empty state)
+                DT::template compute<VAR>(stage, lane, c0.key0(), lo[rb], limit[rb], sl2, p.softcap_l2,
+                                          p.softcap_inv2, qf[rb], m_run[rb], l_run[rb], oacc[rb]);
         if (!c1.valid || c1_new) {
             close(c0);
             pending = true;
@@ -769,10 +800,19 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_balanced_kernel
         advance(c2);
         if (c1_new) {
 #pragma unroll
-            for (int ks = 0; ks < DT::KS; ++ks) qf[ks] = qn[ks];
-            limit = decode_row_limit(p, lane, c0.q_len, c0.L);
-            if constexpr (VAR) lo = decode_row_lo(p, lane, c0.q_len, c0.L);
-            sk = sk_next;
+            for (int rb = 0; rb < RB; ++rb) {
+                if constexpr (QN) {
+#pragma unroll
+                    for (int ks = 0; ks < DT::KS; ++ks) qf[rb][ks] = qn[ks];
+                    sk[rb] = sk_next[rb];
+                } else {
+                    // (the loads complete with this iteration's tile loads)
+                    load_decode_q<HD>(p, lane, c0.q0, c0.q_len * p.g, c0.kh, qf[rb], 16 * rb);
+                    sk[rb] = has_sinks ? sink_l2(p, head_of(c0.kh, rb)) : -INFINITY;
+                }
+                limit[rb] = decode_row_limit(p, lane, c0.q_len, c0.L, 16 * rb);
+                if constexpr (VAR) lo[rb] = decode_row_lo(p, lane, c0.q_len, c0.L, 16 * rb);
+            }
             seg_t0 = 0;
         }
         DT::store(stage, lane, kr, vr);
@@ -1444,8 +1484,8 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
 }
 
 // Merge for the balanced decode schedule: one half-wave per row of a
-// (request, kv head) item, two workgroups of eight half-waves per item (up to
-// 16 rows). The item was covered by waves wave_of(first tile) ..
+// (request, kv head) item, dec_rows / 8 workgroups of eight half-waves per
+// item (dec_rows = 16 RB rows). The item was covered by waves wave_of(first tile) ..
 // wave_of(last tile) (those that own at least one tile); with one wave the
 // output is already final. The item comes from the block index, so the
 // metadata loads are independent of each other.
@@ -1453,10 +1493,11 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
     const int lane = threadIdx.x & 63;
     const int hl = lane & 31;
     const int base_lane = lane & 32;
-    const int64_t item = blockIdx.x >> 1;
+    const int wgs = p.dec_rows >> 3;  // workgroups per item
+    const int64_t item = blockIdx.x / wgs;
     const int r = (int)(item / p.Hkv);
     const int kh = (int)(item % p.Hkv);
-    const int row16 = (int)((blockIdx.x & 1) * 8 + (threadIdx.x >> 5));
+    const int row16 = (int)((blockIdx.x % wgs) * 8 + (threadIdx.x >> 5));  // row within the item
     const int q0 = p.qsl[r];
     const int q_len = p.qsl[r + 1] - q0;
     if (row16 >= q_len * p.g) return;  // whole half-waves leave together
@@ -1479,11 +1520,11 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int j = hl + 32 * c;
-        lsv[c] = (j < np && owns_tiles(wf + j)) ? p.part_lse[(slot0 + j) * 16 + row16] : -INFINITY;
+        lsv[c] = (j < np && owns_tiles(wf + j)) ? p.part_lse[(slot0 + j) * p.dec_rows + row16] : -INFINITY;
         M = fmaxf(M, lsv[c]);
     }
     for (int j = hl + 64; j < np; j += 32)
-        if (owns_tiles(wf + j)) M = fmaxf(M, p.part_lse[(slot0 + j) * 16 + row16]);
+        if (owns_tiles(wf + j)) M = fmaxf(M, p.part_lse[(slot0 + j) * p.dec_rows + row16]);
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float Mu = M == -INFINITY ? 0.f : M;
@@ -1495,7 +1536,7 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
         const int j = j0 + hl;
         float ls;
         if (j0 < 64) ls = lsv[j0 >> 5];
-        else ls = (j < np && owns_tiles(wf + j)) ? p.part_lse[(slot0 + j) * 16 + row16] : -INFINITY;
+        else ls = (j < np && owns_tiles(wf + j)) ? p.part_lse[(slot0 + j) * p.dec_rows + row16] : -INFINITY;
         const float wj = fast_exp2((ls - Mu) * kLog2e);  // 0 for absent partials
         wsum += wj;
         const int cnt = min(32, np - j0);
@@ -1507,7 +1548,7 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
             for (int u = 0; u < 4; ++u) {
                 wk[u] = __shfl(wj, base_lane + min(k + u, cnt - 1));
                 if (k + u >= cnt) wk[u] = 0.f;
-                const float* src = p.part_o + ((slot0 + j0 + min(k + u, cnt - 1)) * 16 + row16) * p.hd;
+                const float* src = p.part_o + ((slot0 + j0 + min(k + u, cnt - 1)) * p.dec_rows + row16) * p.hd;
                 v0[u] = c0 ? *(const f32x4*)(src + 4 * hl) : f32x4{0.f, 0.f, 0.f, 0.f};
                 v1[u] = c1 ? *(const f32x4*)(src + 4 * (hl + 32)) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -1601,17 +1642,33 @@ static hipError_t decode_hd(const FwdParams& p, KvType kv, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int HD, int RB>
+static void decode_balanced_rb(const FwdParams& p, KvType kv, bool var, dim3 grid, hipStream_t s) {
+    const bool paged = p.bt != nullptr;
+    if (kv == KvType::FP8) {
+        if (paged) launch_var((decode_balanced_kernel<HD, true, true, true, RB>),
+                              (decode_balanced_kernel<HD, true, true, false, RB>), var, grid, s, p);
+        else launch_var((decode_balanced_kernel<HD, true, false, true, RB>),
+                        (decode_balanced_kernel<HD, true, false, false, RB>), var, grid, s, p);
+    } else {
+        if (paged) launch_var((decode_balanced_kernel<HD, false, true, true, RB>),
+                              (decode_balanced_kernel<HD, false, true, false, RB>), var, grid, s, p);
+        else launch_var((decode_balanced_kernel<HD, false, false, true, RB>),
+                        (decode_balanced_kernel<HD, false, false, false, RB>), var, grid, s, p);
+    }
+}
+
 template <int HD>
 static hipError_t decode_balanced_hd(const FwdParams& p, KvType kv, hipStream_t s) {
     dim3 grid(p.sk_waves / 4);
     const bool var = uses_var(p);
-    const bool paged = p.bt != nullptr;
-    if (kv == KvType::FP8) {
-        if (paged) launch_var((decode_balanced_kernel<HD, true, true, true>), (decode_balanced_kernel<HD, true, true, false>), var, grid, s, p);
-        else launch_var((decode_balanced_kernel<HD, true, false, true>), (decode_balanced_kernel<HD, true, false, false>), var, grid, s, p);
+    if (p.dec_rows == 16) {
+        decode_balanced_rb<HD, 1>(p, kv, var, grid, s);
+    } else if constexpr (HD <= kDecodeMaxRbHead) {
+        if (p.dec_rows == 32) decode_balanced_rb<HD, 2>(p, kv, var, grid, s);
+        else return hipErrorInvalidValue;
     } else {
-        if (paged) launch_var((decode_balanced_kernel<HD, false, true, true>), (decode_balanced_kernel<HD, false, true, false>), var, grid, s, p);
-        else launch_var((decode_balanced_kernel<HD, false, false, true>), (decode_balanced_kernel<HD, false, false, false>), var, grid, s, p);
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -1626,8 +1683,8 @@ hipError_t launch_decode_balanced(const FwdParams& p, KvType kv, hipStream_t s) 
 }
 
 hipError_t launch_combine_balanced(const FwdParams& p, hipStream_t s) {
-    const int64_t items = (int64_t)p.B * p.Hkv;  // two workgroups (16 row slots) per item
-    hipLaunchKernelGGL(combine_balanced_kernel, dim3((unsigned)(2 * items)), dim3(256), 0, s, p);
+    const int64_t items = (int64_t)p.B * p.Hkv;  // dec_rows / 8 workgroups per item
+    hipLaunchKernelGGL(combine_balanced_kernel, dim3((unsigned)(items * (p.dec_rows / 8))), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

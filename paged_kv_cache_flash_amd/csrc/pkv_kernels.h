@@ -31,6 +31,7 @@ struct FwdParams {
     // balanced decode schedule
     int32_t sk_waves;         // waves sharing the decode tiles (grid = sk_waves / 4 workgroups)
     int32_t* sk_prefix;       // [B+1] per-request tile prefix and total, written by the attention kernel
+    int32_t dec_rows;         // query rows per item slot (16 or 32: 16-row blocks per item)
     // attention variants
     int32_t window_left;      // < 0: no sliding window
     float softcap_l2;         // softcap * log2(e) (> 0), or 0: no soft cap
@@ -64,6 +65,12 @@ constexpr int kDecodeWaves = 4;
 // saturation there; fp8 caches use twice as many) and the largest batch whose
 // schedule each wave derives by itself.
 constexpr int kBalancedWaves = 1024;
+// Balanced decode items hold up to kDecodeMaxRows query rows (q_len x group)
+// as blocks of 16, for head sizes up to kDecodeMaxRbHead (larger heads: 16).
+// (Four blocks overflow the register file of a wave at head size 128; the
+// prefill kernel then serves such items faster.)
+constexpr int kDecodeMaxRows = 32;
+constexpr int kDecodeMaxRbHead = 128;
 constexpr int kBalancedMaxSeqs = 1024;
 // Accelerator complex dies of MI355X; consecutive workgroup ids go to
 // consecutive XCDs, each with its own L2.

@@ -126,6 +126,26 @@ def test_split_plan_and_workspace():
     assert L.pkv_varlen_workspace_size(ctypes.byref(b)) == s * 256 * 8 * (128 + 1) * 4
 
 
+def test_multi_row_decode_plan():
+    # items of q_len x group query rows: up to 16 take one 16-row block per
+    # slot, 17..32 two (paged cache, head size <= 128); beyond 32 rows, or
+    # head size 256, the prefill kernel takes them
+    L = pkv.lib()
+    for q, rows in ((4, 16), (5, 32), (8, 32)):
+        a = good_args(num_tokens=64 * q, max_seqlen_q=q)
+        assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 1024
+        assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == (1024 + 64 * 8) * rows * (128 + 1) * 4 + 65 * 4
+    a = good_args(num_tokens=64 * 9, max_seqlen_q=9)
+    assert L.pkv_varlen_num_splits(ctypes.byref(a)) < 1024  # prefill plan
+    a = good_args(num_tokens=64 * 5, max_seqlen_q=5, head_size=256)
+    assert L.pkv_varlen_num_splits(ctypes.byref(a)) < 1024
+    # an fp8 cache keeps 2048 waves only for single-block items
+    a = good_args(num_tokens=64 * 4, max_seqlen_q=4, kv_dtype=pkv.PKV_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE)
+    assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 2048
+    a.max_seqlen_q, a.num_tokens = 8, 64 * 8
+    assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 1024
+
+
 def test_window_limits_the_split_span():
     # a prefill of 256 new tokens on a 65280-token context, one request, 16
     # work items: without a window it is split into 32 key ranges; with a

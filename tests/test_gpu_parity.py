@@ -132,6 +132,28 @@ def test_decode_parity(case, num_splits):
     run_and_check(prob, num_splits, what=f"decode {case} splits={num_splits}")
 
 
+# Multi-token decode with more than 16 query rows per (request, kv head):
+# the balanced schedule takes items of up to 32 rows as blocks of 16, the
+# prefill kernel larger ones.
+MULTI_ROW_DECODE_CASES = [
+    # (q_lens, ctx_lens, H, Hkv, hd, bs, cache)
+    ([5, 8, 3, 7, 1], [100, 300, 20, 1000, 64], 32, 8, 128, 16, "bf16"),    # g = 4: up to 32 rows
+    ([5, 8, 3, 16, 1], [100, 300, 20, 1000, 64], 32, 8, 128, 16, "bf16"),   # 64 rows: prefill kernel
+    ([2, 3, 4], [700, 33, 2000], 64, 8, 128, 256, "bf16"),                  # g = 8: 16 to 32 rows
+    ([7, 12], [90, 511], 16, 2, 64, 8, "bf16"),                              # g = 8, head 64: 56 and 96 -> prefill
+    ([6, 2, 8], [300, 40, 129], 32, 8, 64, 16, "bf16"),                      # head 64: up to 32 rows
+    ([4, 8, 5], [1023, 260, 77], 32, 8, 128, 16, "fp8"),                     # fp8 cache, up to 32 rows
+    ([8, 8], [4000, 3], 32, 8, 128, 1, "bf16"),                              # page size 1, 32 rows
+]
+
+
+@pytest.mark.parametrize("case", MULTI_ROW_DECODE_CASES)
+def test_multi_row_decode_parity(case):
+    ql, cl, H, Hkv, hd, bs, cache = case
+    prob = workloads.make_problem(250 + sum(ql) + hd + bs, ql, cl, H=H, Hkv=Hkv, hd=hd, bs=bs, cache_dtype=cache)
+    run_and_check(prob, 0, what=f"multi-row decode {case}")
+
+
 PREFILL_CASES = [
     ([37, 130, 5], [0, 0, 0], 8, 2, 128, 16),
     ([200, 64], [300, 17], 32, 8, 128, 16),

@@ -65,6 +65,7 @@ DECODE_CASES = [
     ([1] * 4, [30, 90, 257, 5], 16, 2, 64, 8),
     ([1] * 2, [300, 77], 8, 2, 256, 16),
     ([1, 0, 1], [500, 10, 7], 32, 8, 128, 3),
+    ([6, 8, 3], [200, 900, 40], 32, 8, 128, 16),    # items of up to 32 query rows (two row blocks)
 ]
 
 

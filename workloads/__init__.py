@@ -264,6 +264,17 @@ def paged_decode(seed: int = 2, B: int = 64, lo: int = 512, hi: int = 4096, H: i
                         cache_dtype=cache_dtype)
 
 
+def spec_decode(seed: int = 6, B: int = 64, qlo: int = 2, qhi: int = 16, lo: int = 512, hi: int = 4096,
+                H: int = 32, Hkv: int = 8, hd: int = 128, bs: int = 16) -> Problem:
+    """Multi-token decode (speculative verification): q_len uniform in
+    [qlo, qhi] new tokens per request on a context uniform in [lo, hi]
+    cached tokens, causal over the new tokens."""
+    rng = np.random.default_rng(seed)
+    ql = rng.integers(qlo, qhi, size=B, endpoint=True).astype(np.int32)
+    ctx = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    return make_problem(seed * 1000 + 1, ql, ctx, H=H, Hkv=Hkv, hd=hd, bs=bs)
+
+
 def chunked_prefill(seed: int = 3, B: int = 8, qlo: int = 128, qhi: int = 2048, clo: int = 0, chi: int = 4096,
                     H: int = 32, Hkv: int = 8, hd: int = 128, bs: int = 16) -> Problem:
     """Chunked prefill: new query lengths uniform in [qlo, qhi] appended to
