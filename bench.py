@@ -37,6 +37,11 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+# fp8-q prefill: Q K^T on the fp8 matrix cores, P V on the bf16 ones, equal
+# flops each, so the time at peak is F/2 / 5.0 + F/2 / 2.5 PFLOP/s
+FP8_QK_BF16_PV_PEAK_TFLOPS = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
+PREFILL_WORKLOADS = ("chunked_prefill", "fp8kv_prefill", "fp8_prefill")
 
 # HBM bytes per launch of the dominant kernel, measured with rocprofv3 counters
 # (FETCH_SIZE, WRITE_SIZE) and scaled by the same counters' reading for a plain
@@ -46,7 +51,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
 KERNEL_SOURCES = ["pkv_attn.hip", "pkv_device.h", "pkv_kernels.h"]
 DOMINANT_KERNEL = {"paged_decode": "decode_balanced_kernel", "chunked_prefill": "prefill_kernel",
                    "long_decode": "decode_balanced_kernel", "long_decode_cascade": "decode_balanced_kernel",
-                   "fp8_decode": "decode_balanced_kernel", "spec_decode": "prefill_kernel"}
+                   "fp8_decode": "decode_balanced_kernel", "spec_decode": "prefill_kernel",
+                   "fp8kv_prefill": "prefill_kernel", "fp8_prefill": "prefill_kernel"}
 
 WORKLOADS = {
     "paged_decode": "paged decode, 32/8 heads GQA, head 128, bf16, batch 64, ctx U[512,4096], page 16",
@@ -58,6 +64,10 @@ WORKLOADS = {
     "fp8_decode": "decode over an fp8 e4m3fn cache, bf16 q, batch 128, ctx U[1024,8192], 32/8 heads, head 128",
     "spec_decode": "multi-token decode (speculative verification), batch 64, q_len U[2,16] on ctx U[512,4096], "
                    "32/8 heads, head 128, bf16, page 16",
+    "fp8kv_prefill": "chunked prefill over an fp8 e4m3fn cache, bf16 q, batch 8, new U[128,2048] on cached "
+                     "U[0,4096], 32/8 heads, head 128, page 16, causal",
+    "fp8_prefill": "chunked prefill, fp8 e4m3fn q and cache (QK^T on fp8 MFMA, PV on bf16 MFMA), batch 8, new "
+                   "U[128,2048] on cached U[0,4096], 32/8 heads, head 128, page 16, causal",
 }
 
 
@@ -79,6 +89,10 @@ def make(name, bs, over=None):
         return workloads.fp8_decode(bs=bs or 16)
     if name == "spec_decode":
         return workloads.spec_decode(bs=bs or 16)
+    if name == "fp8kv_prefill":
+        return workloads.chunked_prefill(bs=bs or 16, cache_dtype="fp8")
+    if name == "fp8_prefill":
+        return workloads.chunked_prefill(bs=bs or 16, cache_dtype="fp8", q_dtype="fp8")
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -249,6 +263,7 @@ def main():
     if prob.cache_dtype == "fp8":
         ks = torch.tensor([prob.k_scale], dtype=torch.float32, device=dev)
         vs = torch.tensor([prob.v_scale], dtype=torch.float32, device=dev)
+    qs = torch.tensor([prob.q_scale], dtype=torch.float32, device=dev) if prob.q_dtype == "fp8" else None
     new_rows = prob.new_rows
     k_new, v_new, slots_new = to_dev(prob.kv_src_k[new_rows]), to_dev(prob.kv_src_v[new_rows]), \
         to_dev(prob.kv_slots[new_rows])
@@ -268,13 +283,13 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {R} cache replicas of {cache_bytes / 1e9:.3f} GB resident")
 
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=torch.bfloat16 if prob.q_dtype == "fp8" else q.dtype, device=dev)
     lse = torch.empty((prob.H, prob.T), dtype=torch.float32, device=dev)
     cascade = prob.shared_prefix > 0
     W = args.sliding_window
     sinks_h = np.random.default_rng(12345).normal(1.5, 2.0, prob.H).astype(np.float32) if args.sinks else None
     fwd_kw = dict(softmax_scale=prob.scale, causal=prob.causal, k_scale=ks, v_scale=vs, sliding_window=W,
-                  softcap=args.softcap, sinks=None if sinks_h is None else to_dev(sinks_h))
+                  softcap=args.softcap, sinks=None if sinks_h is None else to_dev(sinks_h), q_scale=qs)
     if not cascade:
         need = pkv.pkv_varlen_workspace_size(q, reps[0][0], reps[0][1], qsl, seq_lens, bt, prob.max_seqlen_q,
                                              prob.max_seqlen_k, prob.scale, prob.causal, args.num_splits, W)
@@ -332,7 +347,7 @@ def main():
         f"{ms_eager:.4f}); attention calls {calls}, main kernel {main_ms / max(calls, 1):.4f} ms avg, "
         f"merge {merge_ms / max(calls, 1):.4f} ms avg")
 
-    decode_like = args.workload != "chunked_prefill"
+    decode_like = args.workload not in PREFILL_WORKLOADS
     # HBM bytes per launch of the dominant kernel from committed counter runs
     # (None unless they were taken on the current kernel sources)
     traffic = None if variants else measured_traffic(args.workload, prob.bs)
@@ -351,8 +366,9 @@ def main():
         value = fl / (ms_step * 1e-3) / 1e12
         metric, unit = "causal prefill TFLOP/s", "TFLOP/s"
         achieved = fl / (main_ms / args.steps * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+        peak = FP8_QK_BF16_PV_PEAK_TFLOPS if prob.q_dtype == "fp8" else BF16_PEAK_TFLOPS
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": traffic,
                     "algorithmic_flops_per_launch": fl}
 
     cpu = None
@@ -371,7 +387,7 @@ def main():
                      sinks=None if sinks_h is None else sinks_h.astype(np.float64))
         ref, ref_lse = oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, prob.seq_lens, prob.block_table,
                                         scale=prob.scale, causal=prob.causal, rows=sample, k_scale=prob.k_scale,
-                                        v_scale=prob.v_scale, **var_o)
+                                        v_scale=prob.v_scale, q_scale=prob.q_scale, **var_o)
         tol = 5e-2 if prob.cache_dtype == "fp8" else 1e-2
         o = out.float().cpu().numpy().astype(np.float64)[sample]
         half_ulp = np.where(np.abs(ref) > 0, np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8), 0)
@@ -394,7 +410,7 @@ def main():
             t1 = time.perf_counter()
             oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, prob.seq_lens, prob.block_table,
                              scale=prob.scale, causal=prob.causal, rows=rows, k_scale=prob.k_scale,
-                             v_scale=prob.v_scale, nthreads=nthr, **var_o)
+                             v_scale=prob.v_scale, nthreads=nthr, q_scale=prob.q_scale, **var_o)
             t_cpu += time.perf_counter() - t1
             n_vis = int(vis[rows].sum())
             done_flops += 4 * prob.hd * prob.H * n_vis
@@ -426,7 +442,7 @@ def main():
            "parallelism": "single GPU"}
     line = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg, "roofline": roofline,
+            "vs_baseline": None, "dtype": "fp8 QK^T, bf16 PV" if prob.q_dtype == "fp8" else "bf16", "data": "synthetic", "config": cfg, "roofline": roofline,
             "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 

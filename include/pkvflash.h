@@ -116,7 +116,8 @@ pkv_status pkv_cache_write(const void* key, const void* value, pkv_dtype src_dty
  *          forward calls only).
  *
  * Layouts: q, out [num_tokens, num_heads, head_size] in q_dtype (out has the
- *          type of q); lse [num_heads, num_tokens] fp32, or NULL;
+ *          type of q, except bf16 for an FP8_E4M3FN q); lse [num_heads,
+ *          num_tokens] fp32, or NULL;
  *          k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_size]
  *          in kv_dtype; block_table int32 rows of block_table_stride entries
  *          (a row may be a strided view: pass the address of its first used
@@ -126,8 +127,14 @@ pkv_status pkv_cache_write(const void* key, const void* value, pkv_dtype src_dty
  *          v_cache are [num_tokens, num_kv_heads, head_size] packed like q and
  *          each request attends to its own new tokens only (seq_lens may be
  *          NULL; it is then taken as q_len).
- * Types:   q_dtype BF16 with kv_dtype BF16 or FP8_E4M3FN; F32 with F32.
- *          FP8 keys/values are multiplied by *k_scale / *v_scale (device fp32).
+ * Types:   q_dtype BF16 with kv_dtype BF16 or FP8_E4M3FN; F32 with F32;
+ *          FP8_E4M3FN with FP8_E4M3FN (head_size 128 only). FP8 keys/values
+ *          are multiplied by *k_scale / *v_scale, an FP8 q by *q_scale (device
+ *          fp32), as the deep-dive page's backend passes q_descale, k_descale
+ *          and v_descale to the forward (FP8 section). With an FP8 q the
+ *          product Q K^T runs on the fp8 matrix cores (exact products, fp32
+ *          sums) and P V on the bf16 ones (P rounded to bf16), whatever the
+ *          shape of the batch.
  * Head size: a multiple of 8, at most 256 (the deep-dive page's backend rule).
  * Split-KV: num_splits 0 lets the library choose from the host sizes, 1 turns
  *          splitting off, > 1 asks for that many KV splits (at most 256). With
@@ -166,6 +173,7 @@ typedef struct pkv_varlen_args {
     int32_t sliding_window; /* 0: no sliding window */
     float softcap;          /* 0: no logits soft cap */
     const float* sinks;     /* [num_heads] device fp32, or NULL */
+    const float* q_scale;   /* FP8 q only: device fp32 */
 } pkv_varlen_args;
 
 /* sizeof(pkv_varlen_args), so bindings can check their mirror of the struct. */

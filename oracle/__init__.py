@@ -125,7 +125,8 @@ def _prep(q, k, v, query_start_loc, seq_lens, block_table, H, Hkv, bs):
 
 
 def attention(q, k, v, query_start_loc, seq_lens=None, block_table=None, *, scale, causal=True,
-              k_scale=1.0, v_scale=1.0, rows=None, nthreads=0, window_left=-1, softcap=0.0, sinks=None):
+              k_scale=1.0, v_scale=1.0, rows=None, nthreads=0, window_left=-1, softcap=0.0, sinks=None,
+              q_scale=1.0):
     """Definition of the varlen (optionally paged) attention forward.
 
     Returns (out [n_rows, H, hd] float64, lse [H, n_rows] float64). ``rows``
@@ -133,7 +134,9 @@ def attention(q, k, v, query_start_loc, seq_lens=None, block_table=None, *, scal
     Variants: ``window_left`` >= 0 limits query position i to keys
     j >= i - window_left; ``softcap`` > 0 maps each scaled score s to
     softcap * tanh(s / softcap); ``sinks`` [H] adds one logit per head to the
-    softmax normaliser (no value row)."""
+    softmax normaliser (no value row). An e4m3fn q (uint8 codes) stands for
+    its decoded values times ``q_scale``; the factor is applied to the scale
+    (each score is linear in q)."""
     q, k, v, qsl, seq_lens, bt, bt_stride, B, T, H, Hkv, hd, bs = _prep(q, k, v, query_start_loc, seq_lens,
                                                                            block_table, None, None, None)
     if rows is None:
@@ -147,7 +150,8 @@ def attention(q, k, v, query_start_loc, seq_lens=None, block_table=None, *, scal
     sk = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float64).reshape(H)
     rc = lib().or_attention_ex(_ptr(q), _code(q), _ptr(k), _ptr(v), _code(k), float(k_scale), float(v_scale),
                                _ptr(qsl), _ptr(seq_lens), _ptr(bt), bt_stride, B, H, Hkv, hd, bs,
-                               float(scale), int(bool(causal)), int(window_left), float(softcap), _ptr(sk),
+                               float(scale) * float(q_scale), int(bool(causal)), int(window_left), float(softcap),
+                               _ptr(sk),
                                _ptr(rows_arr), n, _ptr(out), _ptr(lse), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the problem (H % Hkv != 0 or empty batch)")

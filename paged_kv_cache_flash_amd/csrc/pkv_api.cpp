@@ -75,6 +75,7 @@ pkv_status validate(const pkv_varlen_args* a) {
     if (a->block_table && !a->seq_lens) return fail(PKV_ERR_INVALID_ARG, "a paged cache needs seq_lens");
     if (a->kv_dtype == PKV_FP8_E4M3FN && (!a->k_scale || !a->v_scale))
         return fail(PKV_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    if (a->q_dtype == PKV_FP8_E4M3FN && !a->q_scale) return fail(PKV_ERR_INVALID_ARG, "an fp8 q needs q_scale");
     return ok();
 }
 
@@ -90,8 +91,12 @@ pkv_status validate_sizes(const pkv_varlen_args* a) {
     if (a->head_size <= 0 || a->head_size % 8 != 0 || a->head_size > 256)
         return fail(PKV_ERR_UNSUPPORTED, "head_size %d: must be a multiple of 8 and at most 256", a->head_size);
     const bool ok_types = (a->q_dtype == PKV_BF16 && (a->kv_dtype == PKV_BF16 || a->kv_dtype == PKV_FP8_E4M3FN)) ||
-                          (a->q_dtype == PKV_F32 && a->kv_dtype == PKV_F32);
+                          (a->q_dtype == PKV_F32 && a->kv_dtype == PKV_F32) ||
+                          (a->q_dtype == PKV_FP8_E4M3FN && a->kv_dtype == PKV_FP8_E4M3FN);
     if (!ok_types) return fail(PKV_ERR_UNSUPPORTED, "unsupported (q_dtype, kv_dtype) = (%d, %d)", a->q_dtype, a->kv_dtype);
+    if (a->q_dtype == PKV_FP8_E4M3FN && (a->head_size != 128 || a->num_heads / a->num_kv_heads > kPrefillMaxGroup))
+        return fail(PKV_ERR_UNSUPPORTED, "an fp8 q needs head_size 128 and a group of at most %d heads",
+                    kPrefillMaxGroup);
     if (!std::isfinite(a->softmax_scale)) return fail(PKV_ERR_INVALID_ARG, "softmax_scale is not finite");
     if (a->sliding_window < 0) return fail(PKV_ERR_INVALID_ARG, "sliding_window must be >= 0 (0: no window)");
     if (!(a->softcap >= 0.f) || !std::isfinite(a->softcap))
@@ -138,11 +143,12 @@ Plan make_plan(const pkv_varlen_args* a, bool balanced_ok = true) {
     // the splits only need to cover the span from there to its last key.
     if (a->sliding_window > 0)
         max_k = std::min<int64_t>(max_k, (int64_t)a->sliding_window - 1 + a->max_seqlen_q + 63);
-    const bool mfma = a->q_dtype == PKV_BF16 && mfma_head(a->head_size) && g <= kPrefillMaxGroup;
+    const bool q8 = a->q_dtype == PKV_FP8_E4M3FN;  // fp8 QK^T: the prefill kernel, whatever the shape
+    const bool mfma = (a->q_dtype == PKV_BF16 || q8) && mfma_head(a->head_size) && g <= kPrefillMaxGroup;
     int64_t items;
     int align;
     const int32_t drows = decode_rows(a, (int64_t)a->max_seqlen_q * g);
-    if (balanced_ok && mfma && drows > 0 && a->num_splits == 0 && a->num_seqs <= kBalancedMaxSeqs) {
+    if (balanced_ok && mfma && !q8 && drows > 0 && a->num_splits == 0 && a->num_seqs <= kBalancedMaxSeqs) {
         // balanced decode: balanced_waves() waves share the KV tiles equally
         pl.kind = Kind::DecodeBalanced;
         pl.dec_rows = drows;
@@ -153,7 +159,7 @@ Plan make_plan(const pkv_varlen_args* a, bool balanced_ok = true) {
                        (size_t)(a->num_seqs + 1) * sizeof(int32_t);
         return pl;
     }
-    if (mfma && (int64_t)a->max_seqlen_q * g <= kDecodeRows) {
+    if (mfma && !q8 && (int64_t)a->max_seqlen_q * g <= kDecodeRows) {
         pl.kind = Kind::Decode;
         items = (int64_t)a->num_seqs * a->num_kv_heads;
         align = kDecodeTile * kDecodeWaves;
@@ -256,6 +262,7 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     p.bt = a->block_table;
     p.k_scale = a->k_scale;
     p.v_scale = a->v_scale;
+    p.q_scale = a->q_scale;
     p.bt_stride = a->block_table_stride;
     p.T = a->num_tokens;
     p.B = a->num_seqs;
@@ -299,7 +306,7 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     switch (pl.kind) {
         case Kind::DecodeBalanced: e = launch_decode_balanced(p, kv, s); break;
         case Kind::Decode: e = launch_decode(p, kv, s); break;
-        case Kind::Prefill: e = launch_prefill(p, kv, s); break;
+        case Kind::Prefill: e = launch_prefill(p, kv, a->q_dtype == PKV_FP8_E4M3FN, s); break;
         default: e = launch_generic(p, kv, a->q_dtype == PKV_F32, s); break;
     }
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");

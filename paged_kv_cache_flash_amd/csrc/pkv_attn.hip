@@ -893,6 +893,16 @@ constexpr int pext(int x, int mask) {
 constexpr int popcount(int x) { return x ? (x & 1) + popcount(x >> 1) : 0; }
 constexpr int kTileRows = 64;
 
+// K tiles kept as e4m3fn for the fp8 QK^T MFMA (head size 128): 128-byte
+// rows, 1 KB copy groups of 8 rows with no padding, the 16-byte chunk c of
+// row r at position c ^ sw(r). With this permutation the 16-byte A-operand
+// reads (rows l % 32, chunks picked by l / 32) hit every one of the 64 LDS
+// banks once per 16 lanes.
+struct PfK8 {
+    static constexpr int RP = 128;
+    static __device__ __forceinline__ int sw(int r) { return 2 * ((r >> 1) & 1) ^ ((r >> 2) & 1) ^ 4 * ((r >> 3) & 1); }
+};
+
 // How a prefill workgroup finds the cache rows of a tile's keys.
 //  kPgAny:  any page size; every key is translated through the block table.
 //  kPgWide: the page size is a power of two of at least 16. The 16 keys a
@@ -902,7 +912,11 @@ constexpr int kTileRows = 64;
 constexpr int kPgAny = 0, kPgWide = 1, kPgFlat = 2;
 
 // VAR: the sliding window / soft cap code is compiled in.
-template <int HD, bool FP8, int PG, bool VAR>
+// Q8: q is e4m3fn (with q_scale) over an e4m3fn cache; S^T = K Q^T runs on
+// the fp8 MFMA with K copied into LDS as bytes, PV stays on the bf16 MFMA
+// (V widened to bf16, P rounded to bf16: an e4m3 P would cost up to about
+// 2^-4 of a value row's magnitude per output element).
+template <int HD, bool FP8, int PG, bool VAR, bool Q8>
 __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdParams p) {
     constexpr int NW = kPrefillWaves;           // waves per workgroup
     constexpr int ROWS = prefill_rows(HD);      // query rows per work item
@@ -921,6 +935,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     constexpr int SLOT = TILE / PT::KPI * PT::GP;  // bytes of one K or V tile
     constexpr int ESZ = FP8 ? 1 : 2;            // bytes per cached element
     static_assert(TILE == kTileRows && CPW >= 1 && FCPW >= 1 && KPI == PT::KPI, "");
+    static_assert(!Q8 || (FP8 && HD == 128 && FPR == 8), "the fp8 MFMA mode is built for head size 128");
     // K tile j in k_lds<j % 2>, V tile j in v_lds<j % 2>; four separate arrays
     // so that the compiler sees the copies into one slot are independent of
     // the reads of another and does not wait for them
@@ -984,7 +999,18 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     }
 
     u32x4 qf[KS];
-    {
+    // Q8: bytes 64 ks + 32 hsel + 16 t of the row, t = 0, 1 (B operand of the
+    // fp8 MFMA, k-steps of 64)
+    constexpr int KS8 = HD / 64;
+    u32x4 qf8[KS8][2];
+    if constexpr (Q8) {
+        const uint8_t* qp = (const uint8_t*)p.q + ((int64_t)(q0 + (row_ok ? tl : 0)) * p.H + head) * HD + hsel * 32;
+#pragma unroll
+        for (int ks = 0; ks < KS8; ++ks)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                qf8[ks][t] = row_ok ? *(const u32x4*)(qp + ks * 64 + t * 16) : u32x4{0u, 0u, 0u, 0u};
+    } else {
         const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(q0 + (row_ok ? tl : 0)) * p.H + head) * HD + hsel * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? *(const u32x4*)(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
@@ -994,6 +1020,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         sl2 *= *p.k_scale;
         vsc = *p.v_scale;
     }
+    if constexpr (Q8) sl2 *= *p.q_scale;
     // With the soft cap the scores are scaled and capped in place (log2
     // domain) before the mask, and the softmax then takes them with scale 1.
     const bool capped = VAR && p.softcap_l2 > 0.f;
@@ -1078,12 +1105,18 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         else return q0 + pos;
     };
     u32x4 st_k[NK], st_v[NK];  // fp8 staging
-    auto issue = [&](const void* cache, int t0, const int32_t (&pg)[NP], uint8_t* slot, u32x4 (&st)[NK]) {
+    // (Q8: K tiles go to LDS as bytes, copied like the bf16 tiles: load jj of
+    // wave w moves keys (w FCPW + jj) FKPI .. + 7, 1 KB of whole rows)
+    auto issue = [&](const void* cache, int t0, const int32_t (&pg)[NP], uint8_t* slot, u32x4 (&st)[NK],
+                     bool k_tile) {
 #pragma unroll
         for (int jj = 0; jj < NK; ++jj) {
             // first element of the key's head row
             const int64_t rowe = ((int64_t)row_of(t0, pg, jj) * p.Hkv + kh) * HD;
-            if constexpr (FP8) {
+            if (Q8 && k_tile) {
+                const int chunk = (lane % FPR) ^ PfK8::sw(key_of(jj));
+                copy16_to_lds<0>((const uint8_t*)cache + rowe + chunk * 16, slot + (w * FCPW + jj) * 1024);
+            } else if constexpr (FP8) {
                 st[jj] = *(const u32x4*)((const uint8_t*)cache + rowe + (lane % FPR) * 16);
             } else {
                 const int chunk = (lane % CPR) ^ PT::sw(key_of(jj));
@@ -1109,8 +1142,29 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
 
+    // Q8: per-lane byte offsets of the K fragment (row l % 32 of a 32-key
+    // block, chunk 4 ks + 2 hsel + t at its permuted position)
+    uint32_t koff8[KS8][2];
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            koff8[ks][t] = (lane & 31) * PfK8::RP + 16 * ((4 * ks + 2 * hsel + t) ^ PfK8::sw(lane & 31));
     // S^T = K Q^T for one tile
     auto qk = [&](const uint8_t* kslot, f32x16 (&sacc)[KB]) {
+        if constexpr (Q8) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS8; ++ks)
+                    sacc[kb] = mfma32x32x64_fp8(*(const u32x4*)(kslot + kb * 32 * PfK8::RP + koff8[ks][0]),
+                                                *(const u32x4*)(kslot + kb * 32 * PfK8::RP + koff8[ks][1]),
+                                                qf8[ks][0], qf8[ks][1], sacc[kb]);
+            }
+            return;
+        }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -1216,16 +1270,16 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     {
         int32_t pg0[NP];
         page_of(k_begin, pg0);
-        issue(p.k_cache, k_begin, pg0, k_lds0, st_k);
-        issue(p.v_cache, k_begin, pg0, v_lds0, st_v);
+        issue(p.k_cache, k_begin, pg0, k_lds0, st_k, true);
+        issue(p.v_cache, k_begin, pg0, v_lds0, st_v, false);
         if constexpr (FP8) {
-            land(k_lds0, st_k);  // (waits for its loads)
+            if constexpr (!Q8) land(k_lds0, st_k);  // (waits for its loads)
             land(v_lds0, st_v);
         }
         page_of(k_begin + TILE, pg_v);
         if (n_tiles > 1) {
-            issue(p.k_cache, k_begin + TILE, pg_v, k_lds1, st_k);
-            if constexpr (FP8) land(k_lds1, st_k);
+            issue(p.k_cache, k_begin + TILE, pg_v, k_lds1, st_k, true);
+            if constexpr (FP8 && !Q8) land(k_lds1, st_k);
         }
         page_of(k_begin + 2 * TILE, pg_k);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1249,8 +1303,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
 #pragma unroll
         for (int jj = 0; jj < NP; ++jj) pg_kk[jj] = pg_k[jj];
         if constexpr (!LAST) {
-            if (load_k) issue(p.k_cache, t0 + 2 * TILE, pg_k, k_here, st_k);
-            issue(p.v_cache, t0 + TILE, pg_v, v_next, st_v);
+            if (load_k) issue(p.k_cache, t0 + 2 * TILE, pg_k, k_here, st_k, true);
+            issue(p.v_cache, t0 + TILE, pg_v, v_next, st_v, false);
             if (i + 3 < n_tiles) page_of(t0 + 3 * TILE, pg_k);
         }
         rescale(mx);
@@ -1265,7 +1319,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         if constexpr (!LAST) {
             mx = rowmax(sn);
             if constexpr (FP8) {
-                if (load_k) land(k_here, st_k);
+                if (!Q8 && load_k) land(k_here, st_k);
                 land(v_next, st_v);
             }
 #pragma unroll
@@ -1698,29 +1752,39 @@ hipError_t launch_decode(const FwdParams& p, KvType kv, hipStream_t s) {
 }
 
 template <int HD>
-static hipError_t prefill_hd(const FwdParams& p, KvType kv, hipStream_t s) {
+static hipError_t prefill_hd(const FwdParams& p, KvType kv, bool q8, hipStream_t s) {
     const int64_t streams_per_xcd = ((int64_t)p.B * p.Hkv + kXcds - 1) / kXcds;
     dim3 grid((unsigned)(streams_per_xcd * kXcds * p.n_qtiles), p.num_splits);
     const dim3 block(64 * kPrefillWaves);
     const int pg = !p.bt ? kPgFlat : (p.bs_shift >= 4 ? kPgWide : kPgAny);
     const bool var = uses_var(p);
+    if constexpr (HD == 128) {
+        if (q8) {  // e4m3fn q over an e4m3fn cache
+            if (kv != KvType::FP8) return hipErrorInvalidValue;
+            if (pg == kPgFlat) launch_var((prefill_kernel<HD, true, kPgFlat, true, true>), (prefill_kernel<HD, true, kPgFlat, false, true>), var, grid, s, p);
+            else if (pg == kPgWide) launch_var((prefill_kernel<HD, true, kPgWide, true, true>), (prefill_kernel<HD, true, kPgWide, false, true>), var, grid, s, p);
+            else launch_var((prefill_kernel<HD, true, kPgAny, true, true>), (prefill_kernel<HD, true, kPgAny, false, true>), var, grid, s, p);
+            return hipGetLastError();
+        }
+    }
+    if (q8) return hipErrorInvalidValue;
     if (kv == KvType::FP8) {
-        if (pg == kPgFlat) launch_var((prefill_kernel<HD, true, kPgFlat, true>), (prefill_kernel<HD, true, kPgFlat, false>), var, grid, s, p);
-        else if (pg == kPgWide) launch_var((prefill_kernel<HD, true, kPgWide, true>), (prefill_kernel<HD, true, kPgWide, false>), var, grid, s, p);
-        else launch_var((prefill_kernel<HD, true, kPgAny, true>), (prefill_kernel<HD, true, kPgAny, false>), var, grid, s, p);
+        if (pg == kPgFlat) launch_var((prefill_kernel<HD, true, kPgFlat, true, false>), (prefill_kernel<HD, true, kPgFlat, false, false>), var, grid, s, p);
+        else if (pg == kPgWide) launch_var((prefill_kernel<HD, true, kPgWide, true, false>), (prefill_kernel<HD, true, kPgWide, false, false>), var, grid, s, p);
+        else launch_var((prefill_kernel<HD, true, kPgAny, true, false>), (prefill_kernel<HD, true, kPgAny, false, false>), var, grid, s, p);
     } else {
-        if (pg == kPgFlat) launch_var((prefill_kernel<HD, false, kPgFlat, true>), (prefill_kernel<HD, false, kPgFlat, false>), var, grid, s, p);
-        else if (pg == kPgWide) launch_var((prefill_kernel<HD, false, kPgWide, true>), (prefill_kernel<HD, false, kPgWide, false>), var, grid, s, p);
-        else launch_var((prefill_kernel<HD, false, kPgAny, true>), (prefill_kernel<HD, false, kPgAny, false>), var, grid, s, p);
+        if (pg == kPgFlat) launch_var((prefill_kernel<HD, false, kPgFlat, true, false>), (prefill_kernel<HD, false, kPgFlat, false, false>), var, grid, s, p);
+        else if (pg == kPgWide) launch_var((prefill_kernel<HD, false, kPgWide, true, false>), (prefill_kernel<HD, false, kPgWide, false, false>), var, grid, s, p);
+        else launch_var((prefill_kernel<HD, false, kPgAny, true, false>), (prefill_kernel<HD, false, kPgAny, false, false>), var, grid, s, p);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(const FwdParams& p, KvType kv, hipStream_t s) {
+hipError_t launch_prefill(const FwdParams& p, KvType kv, bool q8, hipStream_t s) {
     switch (p.hd) {
-        case 64: return prefill_hd<64>(p, kv, s);
-        case 128: return prefill_hd<128>(p, kv, s);
-        case 256: return prefill_hd<256>(p, kv, s);
+        case 64: return prefill_hd<64>(p, kv, q8, s);
+        case 128: return prefill_hd<128>(p, kv, q8, s);
+        case 256: return prefill_hd<256>(p, kv, q8, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -9,6 +9,9 @@
 //      element i%4 of the 8-byte chunk addressed by lane 4e + i/4 of the group;
 //      i.e. lanes 4e..4e+3 address row e of a 4 x 16 block and lane i receives
 //      column i.
+//  v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3): lane l holds A row l%32 and B
+//      column l%32, 32 bytes each whose k index depends only on (l/32, byte),
+//      the same for A and B; C as for the 32x32 bf16 MFMA.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,6 +26,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -35,6 +39,14 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    c, 0, 0, 0);
+}
+
+// S += A B on e4m3fn operands (32 bytes per lane each, k layout as noted at
+// the top), fp32 accumulation; no block scaling.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c) {
+    const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // Transposed 4 x b16 read from LDS (see the layout note at the top).

@@ -19,6 +19,7 @@ struct FwdParams {
     const int32_t* bt;        // block table or nullptr (flat)
     const float* k_scale;     // fp8 only
     const float* v_scale;
+    const float* q_scale;     // e4m3fn q only
     int64_t bt_stride;
     int64_t T;
     int32_t B, H, Hkv, g, hd, bs;
@@ -45,7 +46,7 @@ enum class KvType { BF16, FP8, F32 };
 hipError_t launch_decode(const FwdParams& p, KvType kv, hipStream_t s);
 hipError_t launch_decode_balanced(const FwdParams& p, KvType kv, hipStream_t s);
 hipError_t launch_combine_balanced(const FwdParams& p, hipStream_t s);
-hipError_t launch_prefill(const FwdParams& p, KvType kv, hipStream_t s);
+hipError_t launch_prefill(const FwdParams& p, KvType kv, bool q8, hipStream_t s);
 hipError_t launch_generic(const FwdParams& p, KvType kv, bool q_f32, hipStream_t s);
 hipError_t launch_combine(const FwdParams& p, bool out_f32, hipStream_t s);
 hipError_t launch_merge(void* out, float* out_lse, const void* po, const float* plse, const void* so,

@@ -40,7 +40,9 @@ class GpuProblem:
         self.prob = prob
         self.q = to_dev(prob.q)
         self.qsl = to_dev(prob.query_start_loc)
-        self.k_scale = self.v_scale = None
+        self.k_scale = self.v_scale = self.q_scale = None
+        if prob.q_dtype == "fp8":
+            self.q_scale = torch.tensor([prob.q_scale], dtype=torch.float32, device=DEV)
         if prob.cache_dtype == "fp8":
             self.k_scale = torch.tensor([prob.k_scale], dtype=torch.float32, device=DEV)
             self.v_scale = torch.tensor([prob.v_scale], dtype=torch.float32, device=DEV)
@@ -76,7 +78,7 @@ class GpuProblem:
                                   p.max_seqlen_k if p.paged else p.max_seqlen_q, p.scale,
                                   causal=p.causal if causal is None else causal, k_scale=self.k_scale,
                                   v_scale=self.v_scale, num_splits=num_splits, return_lse=True,
-                                  sliding_window=sliding_window, softcap=softcap,
+                                  sliding_window=sliding_window, softcap=softcap, q_scale=self.q_scale,
                                   sinks=None if sinks is None else to_dev(np.asarray(sinks, np.float32)))
 
 
@@ -105,11 +107,11 @@ def oracle_attention(prob, rows=None, causal=None, caches=None, sliding_window=0
     if not prob.paged:
         flat = np.concatenate(prob.pos_rows)
         return oracle.attention(prob.q, prob.kv_src_k[flat], prob.kv_src_v[flat], prob.query_start_loc,
-                                scale=prob.scale, causal=causal, rows=rows, **var)
+                                scale=prob.scale, causal=causal, rows=rows, q_scale=prob.q_scale, **var)
     kc, vc = caches if caches is not None else oracle_cache(prob)
     return oracle.attention(prob.q, kc, vc, prob.query_start_loc, prob.seq_lens, prob.block_table,
                             scale=prob.scale, causal=causal, rows=rows, k_scale=prob.k_scale,
-                            v_scale=prob.v_scale, **var)
+                            v_scale=prob.v_scale, q_scale=prob.q_scale, **var)
 
 
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:

@@ -62,6 +62,8 @@ def test_valid_args_pass():
     assert check(good_args(q_dtype=pkv.PKV_F32, kv_dtype=pkv.PKV_F32, head_size=16)) == pkv.PKV_OK
     assert check(good_args(block_table=None, seq_lens=None, max_seqlen_q=8)) == pkv.PKV_OK
     assert check(good_args(num_tokens=0, q=None)) == pkv.PKV_OK  # empty batch is a no-op
+    assert check(good_args(q_dtype=pkv.PKV_FP8_E4M3FN, kv_dtype=pkv.PKV_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE,
+                           q_scale=FAKE)) == pkv.PKV_OK
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -81,11 +83,16 @@ def test_valid_args_pass():
     (dict(num_tokens=100, num_seqs=64, max_seqlen_q=1), pkv.PKV_ERR_INVALID_ARG),
     (dict(kv_dtype=pkv.PKV_FP8_E4M3FN), pkv.PKV_ERR_INVALID_ARG),  # fp8 without scales
     (dict(q_dtype=pkv.PKV_F32), pkv.PKV_ERR_UNSUPPORTED),  # f32 q with bf16 cache
-    (dict(q_dtype=pkv.PKV_FP8_E4M3FN), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(q_dtype=pkv.PKV_FP8_E4M3FN), pkv.PKV_ERR_UNSUPPORTED),  # fp8 q over a bf16 cache
     (dict(num_splits=-1), pkv.PKV_ERR_INVALID_ARG),
     (dict(num_splits=300), pkv.PKV_ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
     (dict(sliding_window=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(q_dtype=pkv.PKV_FP8_E4M3FN, kv_dtype=pkv.PKV_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE),
+     pkv.PKV_ERR_INVALID_ARG),  # fp8 q without q_scale
+    (dict(q_dtype=pkv.PKV_FP8_E4M3FN, q_scale=FAKE), pkv.PKV_ERR_UNSUPPORTED),  # fp8 q over a bf16 cache
+    (dict(q_dtype=pkv.PKV_FP8_E4M3FN, kv_dtype=pkv.PKV_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE, q_scale=FAKE,
+          head_size=64), pkv.PKV_ERR_UNSUPPORTED),
     (dict(softcap=-1.0), pkv.PKV_ERR_INVALID_ARG),
     (dict(softcap=float("inf")), pkv.PKV_ERR_INVALID_ARG),
     (dict(softcap=float("nan")), pkv.PKV_ERR_INVALID_ARG),

@@ -611,3 +611,38 @@ def test_huge_softcap_approaches_no_cap():
     b = _oracle_variant(prob, True, softcap=1e7)
     np.testing.assert_allclose(b[0], a[0], rtol=0, atol=1e-9)
     np.testing.assert_allclose(b[1], a[1], rtol=0, atol=1e-9)
+
+
+# ------------------------------------------------- e4m3fn q with q_scale
+
+def test_fp8_q_equals_decoded_q_times_scale():
+    """An e4m3fn q stands for decode(code) * q_scale: with a power-of-two
+    q_scale the decoded, scaled values are exact in float32, and attention
+    over them (q given as float32) must agree with attention over the codes,
+    and with the global-matrix brute force."""
+    prob = workloads.make_problem(53, [7, 1, 12], [0, 9, 30], H=4, Hkv=2, hd=16, bs=4, q_dtype="fp8",
+                                  cache_dtype="fp8")
+    assert prob.q.dtype == np.uint8 and prob.q_scale != 1.0
+    assert math.log2(prob.q_scale) == int(math.log2(prob.q_scale))
+    kc, vc = prob.empty_cache()
+    kc, vc = oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc, vc, prob.kv_slots, prob.bs,
+                                k_scale=prob.k_scale, v_scale=prob.v_scale)
+    table = np.array([oracle.decode_e4m3fn(c) for c in range(256)])
+    qf = (table[prob.q] * prob.q_scale).astype(np.float32)
+    assert np.array_equal(qf.astype(np.float64), table[prob.q] * prob.q_scale)
+    kw = dict(scale=prob.scale, k_scale=prob.k_scale, v_scale=prob.v_scale)
+    a = oracle.attention(prob.q, kc, vc, prob.query_start_loc, prob.seq_lens, prob.block_table,
+                         q_scale=prob.q_scale, **kw)
+    b = oracle.attention(qf, kc, vc, prob.query_start_loc, prob.seq_lens, prob.block_table, **kw)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-13)
+    # brute force over the decoded cache contents
+    loc = prob.flat_kv()[2]
+    dec_k = table[kc].reshape(-1, prob.Hkv, prob.hd) * prob.k_scale
+    dec_v = table[vc].reshape(-1, prob.Hkv, prob.hd) * prob.v_scale
+    slots = np.concatenate([prob.kv_slots[rows] for rows in prob.pos_rows])
+    b_out, b_lse = global_attention(qf, dec_k[slots].astype(np.float32), dec_v[slots].astype(np.float32),
+                                    prob.query_start_loc, loc, scale=prob.scale, causal=True, H=prob.H,
+                                    Hkv=prob.Hkv)
+    np.testing.assert_allclose(a[0], b_out, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(a[1], b_lse, rtol=0, atol=1e-6)

@@ -114,6 +114,7 @@ class Problem:
     poison_block: int = -1
     k_scale: float = 1.0
     v_scale: float = 1.0
+    q_scale: float = 1.0          # an e4m3fn q holds q / q_scale
     shared_prefix: int = 0
 
     @property
@@ -177,7 +178,18 @@ def make_problem(seed: int, q_lens, ctx_lens, *, H: int, Hkv: int, hd: int, bs: 
     if scale is None:
         scale = 1.0 / np.sqrt(hd)
     rng = np.random.default_rng(seed)
-    q = _draw(rng, (T, H, hd), q_dtype)
+    q_scale = 1.0
+    if q_dtype == "fp8":
+        # e4m3fn codes of N(0, 1) / q_scale, q_scale the power of two that
+        # puts the largest |q| just under the e4m3fn maximum (448); the
+        # rounding is torch's float8_e4m3fn cast
+        import torch
+        qf = _draw(rng, (T, H, hd), "f32")
+        amax = float(np.abs(qf).max()) if qf.size else 1.0
+        q_scale = float(2.0 ** np.ceil(np.log2(max(amax, 1e-30) / 448.0)))
+        q = torch.from_numpy(qf / np.float32(q_scale)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    else:
+        q = _draw(rng, (T, H, hd), q_dtype)
     if shared_prefix:
         assert paged and shared_prefix % bs == 0 and np.all(ctx_lens >= shared_prefix)
     n_rows = int(seq_lens.sum()) - (B - 1) * shared_prefix if B else 0
@@ -197,7 +209,7 @@ def make_problem(seed: int, q_lens, ctx_lens, *, H: int, Hkv: int, hd: int, bs: 
     prob = Problem(B=B, H=H, Hkv=Hkv, hd=hd, bs=bs, q_lens=q_lens, ctx_lens=ctx_lens, seq_lens=seq_lens,
                    query_start_loc=qsl, q=q, q_dtype=q_dtype, kv_dtype=kv_dtype, cache_dtype=cache_dtype,
                    scale=float(scale), causal=causal, paged=paged, kv_src_k=ksrc, kv_src_v=vsrc,
-                   new_rows=new_rows, pos_rows=pos_rows, shared_prefix=shared_prefix)
+                   new_rows=new_rows, pos_rows=pos_rows, shared_prefix=shared_prefix, q_scale=q_scale)
     if cache_dtype == "fp8":
         prob.k_scale = float(np.float32(np.abs(storage_to_f32(ksrc)).max() / np.float32(448.0)))
         prob.v_scale = float(np.float32(np.abs(storage_to_f32(vsrc)).max() / np.float32(448.0)))
@@ -276,13 +288,15 @@ def spec_decode(seed: int = 6, B: int = 64, qlo: int = 2, qhi: int = 16, lo: int
 
 
 def chunked_prefill(seed: int = 3, B: int = 8, qlo: int = 128, qhi: int = 2048, clo: int = 0, chi: int = 4096,
-                    H: int = 32, Hkv: int = 8, hd: int = 128, bs: int = 16) -> Problem:
+                    H: int = 32, Hkv: int = 8, hd: int = 128, bs: int = 16, q_dtype: str = "bf16",
+                    cache_dtype: str = "bf16") -> Problem:
     """Chunked prefill: new query lengths uniform in [qlo, qhi] appended to
     cached prefixes uniform in [clo, chi]; causal over local positions."""
     rng = np.random.default_rng(seed)
     ql = rng.integers(qlo, qhi, size=B, endpoint=True).astype(np.int32)
     cl = rng.integers(clo, chi, size=B, endpoint=True).astype(np.int32)
-    return make_problem(seed * 1000 + 1, ql, cl, H=H, Hkv=Hkv, hd=hd, bs=bs)
+    return make_problem(seed * 1000 + 1, ql, cl, H=H, Hkv=Hkv, hd=hd, bs=bs, q_dtype=q_dtype,
+                        cache_dtype=cache_dtype)
 
 
 def long_decode(seed: int = 4, B: int = 4, L: int = 131072, H: int = 64, Hkv: int = 8, hd: int = 128,
