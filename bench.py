@@ -80,7 +80,7 @@ def make(name, bs, over=None):
     if name == "paged_decode":
         return workloads.paged_decode(bs=bs or 16, **(over or {}))
     if name == "chunked_prefill":
-        return workloads.chunked_prefill()
+        return workloads.chunked_prefill(bs=bs or 16)
     if name == "long_decode":
         return workloads.long_decode()
     if name == "long_decode_cascade":
@@ -192,7 +192,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="paged_decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--block-size", type=int, default=0, help="page size for paged_decode / fp8_decode")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="page size (default 16; a page as long as the longest request makes the KV contiguous)")
     ap.add_argument("--batch", type=int, default=0, help="paged_decode: requests (default 64)")
     ap.add_argument("--heads", type=int, default=0, help="paged_decode: query heads (default 32)")
     ap.add_argument("--kv-heads", type=int, default=0, help="paged_decode: kv heads (default 8)")
@@ -429,6 +430,8 @@ def main():
     if over or (args.block_size and args.workload == "paged_decode"):
         desc = (f"paged decode, {prob.H}/{prob.Hkv} heads, head {prob.hd}, bf16, batch {prob.B}, "
                 f"ctx U[512,4096], page {prob.bs}")
+    if prob.bs != 16 and "page 16" in desc:
+        desc = desc.replace("page 16", f"page {prob.bs}")
     if W > 0:
         desc += f", sliding window {W}"
     if args.softcap > 0:
