@@ -1311,12 +1311,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         u32x4 pf[2 * KB];
         if constexpr (!LAST) qk(k_next, sn);
         expo(sc, pf);
-        if constexpr (!LAST) {
-            cap(sn);
-            mask(t0 + TILE, sn);
-        }
         pv(v_here, pf);
         if constexpr (!LAST) {
+            // (the mask branch comes after PV so that the S^T MFMAs of tile
+            // i+1, the exponentials and the PV MFMAs of tile i share one
+            // basic block for the scheduler)
+            cap(sn);
+            mask(t0 + TILE, sn);
             mx = rowmax(sn);
             if constexpr (FP8) {
                 if (!Q8 && load_k) land(k_here, st_k);
