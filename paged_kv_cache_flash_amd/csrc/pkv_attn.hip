@@ -1259,9 +1259,11 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     // Pipeline, tile i in iteration i. K tile j and V tile j are copied into
     // slot j % 2: K(i+2) and V(i+1) are issued at the start of iteration i and
     // land (barrier) at its end, so each copy has a whole iteration to arrive.
-    // Inside the iteration the S^T MFMAs of tile i+1 are issued next to the
-    // exponentials of tile i, and the PV MFMAs of tile i next to the row
-    // maximum of tile i+1, so the matrix cores and the vector ALUs overlap.
+    // Inside the iteration the S^T MFMAs of tile i+1 and the PV MFMAs of tile
+    // i are issued next to the exponentials of tile i, so the matrix cores
+    // and the vector ALUs overlap; the mask of tile i+1, its row maximum and
+    // the lazy-rescale decision for it follow, after PV, so that their
+    // branches stay out of that block.
     const int n_tiles = (k_end - k_begin + TILE - 1) / TILE;
     f32x16 s_a[KB], s_b[KB];
     float mx;
@@ -1288,6 +1290,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         cap(s_a);
         mask(k_begin, s_a);
         mx = rowmax(s_a);
+        rescale(mx);
         __syncthreads();
     }
     auto iteration = [&](auto par, auto last, int i, f32x16 (&sc)[KB], f32x16 (&sn)[KB]) {
@@ -1307,7 +1310,6 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
             issue(p.v_cache, t0 + TILE, pg_v, v_next, st_v, false);
             if (i + 3 < n_tiles) page_of(t0 + 3 * TILE, pg_k);
         }
-        rescale(mx);
         u32x4 pf[2 * KB];
         if constexpr (!LAST) qk(k_next, sn);
         expo(sc, pf);
@@ -1319,6 +1321,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
             cap(sn);
             mask(t0 + TILE, sn);
             mx = rowmax(sn);
+            rescale(mx);  // (here rather than before the exponentials: its branch stays out of that block)
             if constexpr (FP8) {
                 if (!Q8 && load_k) land(k_here, st_k);
                 land(v_next, st_v);
