@@ -186,6 +186,68 @@ def visible_flops(prob, window=0):
     return 4 * prob.hd * prob.H * int(visible_keys(prob, window).sum())
 
 
+def cascade_sweep():
+    """Plain against cascade decode (64/8 heads, head 128, bf16, page 256) on
+    batches whose requests share a prefix, each form timed as one HIP graph of
+    30 forwards over 3 cache replicas used in turn, and the library's choice
+    (pkv_cascade_choose) with its predicted times."""
+    import torch
+
+    import paged_kv_cache_flash_amd as pkv
+    import workloads
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+    for B, L, P in ((4, 131072, 32768), (4, 131072, 49152), (4, 131072, 65536), (4, 131072, 98304),
+                    (8, 131072, 98304), (2, 262144, 196608), (8, 65536, 49152), (4, 131072, 8192),
+                    (8, 16384, 8192), (16, 8192, 4096), (16, 4096, 512), (32, 8192, 2048), (64, 2048, 1024)):
+        prob = workloads.long_decode(B=B, L=L, shared_prefix=P)
+        reps = []
+        for _ in range(3):
+            kc, vc = prob.empty_cache()
+            kc, vc = to_dev(kc), to_dev(vc)
+            for c0 in range(0, len(prob.kv_src_k), 1 << 20):
+                rr = np.arange(c0, min(len(prob.kv_src_k), c0 + (1 << 20)))
+                pkv.pkv_cache_write(to_dev(prob.kv_src_k[rr]), to_dev(prob.kv_src_v[rr]), kc, vc,
+                                    to_dev(prob.kv_slots[rr]))
+            reps.append((kc, vc))
+        q, qsl, sl, bt = to_dev(prob.q), to_dev(prob.query_start_loc), to_dev(prob.seq_lens), to_dev(prob.block_table)
+        out = torch.empty_like(q)
+        ws = torch.empty(pkv.pkv_varlen_workspace_size(q, reps[0][0], reps[0][1], qsl, sl, bt, prob.max_seqlen_q,
+                                                       prob.max_seqlen_k, prob.scale), dtype=torch.uint8, device=dev)
+        forms = {
+            "plain": lambda i: pkv.pkv_varlen_fwd(q, reps[i % 3][0], reps[i % 3][1], qsl, sl, bt, prob.max_seqlen_q,
+                                                  prob.max_seqlen_k, prob.scale, out=out, workspace=ws),
+            "cascade": lambda i: pkv.cascade_attention(q, reps[i % 3][0], reps[i % 3][1], qsl, sl, bt, P,
+                                                       prob.max_seqlen_q, prob.max_seqlen_k, prob.scale, out=out),
+        }
+        us = {}
+        for name, f in forms.items():
+            for i in range(4):
+                f(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(30):
+                    f(i)
+            g.replay()
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            us[name] = (time.perf_counter() - t) / 30 * 1e6
+        use, tp, tc = pkv.use_cascade_attention(P, prob.seq_lens, prob.Hkv, prob.hd)
+        print(json.dumps({"batch": B, "seq_len": L, "shared_prefix": P, "plain_us": round(us["plain"], 1),
+                          "cascade_us": round(us["cascade"], 1), "model_plain_us": round(tp, 1),
+                          "model_cascade_us": round(tc, 1), "chosen": "cascade" if use else "plain",
+                          "faster": "cascade" if us["cascade"] < us["plain"] else "plain"}), flush=True)
+        del reps
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,10 +273,16 @@ def main():
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="only summarise rocprofv3 --pmc output of this workload into a traffic line")
     ap.add_argument("--calibrate-bytes", type=int, default=1 << 30, help="bytes of the copy in the calibration runs")
+    ap.add_argument("--cascade-sweep", action="store_true",
+                    help="only time plain against cascade decode on shared-prefix batches, next to the library's "
+                         "cascade choice (one JSON line per batch)")
     args = ap.parse_args()
 
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.cascade_sweep:
+        cascade_sweep()
         return
     if args.calibrate_copy:
         import torch

@@ -213,6 +213,26 @@ pkv_status pkv_merge_attn_states(void* out, float* out_lse, const void* prefix_o
                                  const void* suffix_out, const float* suffix_lse, int64_t num_tokens,
                                  int32_t num_heads, int32_t head_size, pkv_dtype dtype, void* stream);
 
+/* Whether to run a batch whose requests share their first common_prefix_len
+ * KV tokens (the same pages) as a cascade: a prefix pass, a suffix pass and
+ * pkv_merge_attn_states. The deep-dive page's decision (cascade attention
+ * section) first rules it out for a prefix under 256 tokens and for sliding
+ * windows; its remaining test, a performance model, is not printed, and its
+ * request-count rule (fewer than 8 requests: no) is that model's stand-in for
+ * its own kernels. Here a model of this library's decode kernels takes both
+ * places, fitted to MI355X measurements: both forms read the unique keys
+ * (the prefix once, every suffix) at 5.2 TB/s; the plain form also re-reads
+ * the shared pages once per further request, and the 256 MB last-level cache
+ * serves most of those: the share that reaches HBM grows from 0 at 0.55 GB
+ * of re-read bytes to 35% at 1.2 GB and beyond; the cascade adds 50 us for
+ * its extra launches (prefix-pass merge, final merge). Bytes per key:
+ * num_kv_heads * head_size * 2 * element bytes.
+ * host_seq_lens: num_seqs KV lengths in host memory. Writes 1 (cascade) or 0
+ * to *use_cascade and, when not NULL, the two predicted times in us.        */
+pkv_status pkv_cascade_choose(int32_t common_prefix_len, int32_t num_seqs, const int32_t* host_seq_lens,
+                              int32_t num_kv_heads, int32_t head_size, pkv_dtype kv_dtype, int32_t sliding_window,
+                              int32_t* use_cascade, double* t_plain_us, double* t_cascade_us);
+
 /* ------------------------------------------------------------------ utilities */
 
 /* Message for the last error on this thread ("" if none). */

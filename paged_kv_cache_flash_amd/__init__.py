@@ -68,7 +68,8 @@ class pkv_varlen_args(ctypes.Structure):
 
 
 EXPORTS = ("pkv_cache_write", "pkv_varlen_args_size", "pkv_varlen_check", "pkv_varlen_num_splits",
-           "pkv_varlen_workspace_size", "pkv_varlen_fwd", "pkv_merge_attn_states", "pkv_last_error",
+           "pkv_varlen_workspace_size", "pkv_varlen_fwd", "pkv_merge_attn_states", "pkv_cascade_choose",
+           "pkv_last_error",
            "pkv_version", "pkv_timing_enable", "pkv_timing_collect")
 
 _lib = None
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_varlen_fwd.argtypes = [ctypes.POINTER(pkv_varlen_args), vp]
     L.pkv_merge_attn_states.restype = i32
     L.pkv_merge_attn_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
+    L.pkv_cascade_choose.restype = i32
+    L.pkv_cascade_choose.argtypes = [i32, i32, vp, i32, i32, i32, i32, vp, vp, vp]
     L.pkv_last_error.restype = ctypes.c_char_p
     L.pkv_last_error.argtypes = []
     L.pkv_version.restype = i32
@@ -260,6 +263,20 @@ def pkv_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suff
                                        _ptr(suffix_out), _ptr(suffix_lse), T, H, hd, _dtype_code(prefix_out),
                                        _stream(stream)))
     return out
+
+
+def use_cascade_attention(common_prefix_len, seq_lens, num_kv_heads, head_size, kv_dtype=PKV_BF16,
+                          sliding_window=0):
+    """Whether the cascade form is predicted to be faster (pkv_cascade_choose); seq_lens is a host
+    sequence of KV lengths. Returns (use, predicted plain us, predicted cascade us)."""
+    import numpy as np
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    use = ctypes.c_int32(0)
+    tp, tc = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    _check(lib().pkv_cascade_choose(int(common_prefix_len), len(sl), sl.ctypes.data_as(ctypes.c_void_p),
+                                    int(num_kv_heads), int(head_size), int(kv_dtype), int(sliding_window),
+                                    ctypes.byref(use), ctypes.byref(tp), ctypes.byref(tc)))
+    return bool(use.value), tp.value, tc.value
 
 
 def cascade_attention(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, common_prefix_len,

@@ -373,6 +373,42 @@ pkv_status pkv_merge_attn_states(void* out, float* out_lse, const void* prefix_o
     return ok();
 }
 
+pkv_status pkv_cascade_choose(int32_t common_prefix_len, int32_t num_seqs, const int32_t* host_seq_lens,
+                              int32_t num_kv_heads, int32_t head_size, pkv_dtype kv_dtype, int32_t sliding_window,
+                              int32_t* use_cascade, double* t_plain_us, double* t_cascade_us) {
+    // decode read rate, fixed cost of the cascade's extra launches, and the
+    // share of the plain form's prefix re-reads that reach HBM (the 256 MB
+    // last-level cache serves the rest): 0 up to 0.55 GB of re-read bytes,
+    // rising by 1 per 1.8 GB to at most 35%; all fitted to measurements on
+    // MI355X (13 shared-prefix decode batches)
+    constexpr double kBytesPerUs = 5.2e6;
+    constexpr double kCascadeFixedUs = 50.0;
+    constexpr double kRereadFree = 0.55e9, kRereadSlope = 1.8e9, kRereadMissMax = 0.35;
+    constexpr int32_t kMinPrefix = 256;
+    if (!use_cascade || num_seqs < 0 || (num_seqs > 0 && !host_seq_lens) || num_kv_heads <= 0 || head_size <= 0 ||
+        common_prefix_len < 0 || sliding_window < 0)
+        return fail(PKV_ERR_INVALID_ARG, "invalid cascade query");
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3FN && kv_dtype != PKV_F32)
+        return fail(PKV_ERR_UNSUPPORTED, "unknown kv_dtype %d", (int)kv_dtype);
+    const double per_key = 2.0 * num_kv_heads * head_size * (kv_dtype == PKV_FP8_E4M3FN ? 1 : kv_dtype == PKV_F32 ? 4 : 2);
+    int64_t keys = 0;
+    bool prefix_fits = num_seqs > 0;
+    for (int32_t r = 0; r < num_seqs; ++r) {
+        if (host_seq_lens[r] < 0) return fail(PKV_ERR_INVALID_ARG, "negative seq_lens[%d]", r);
+        keys += host_seq_lens[r];
+        prefix_fits = prefix_fits && host_seq_lens[r] > common_prefix_len;  // every request keeps a suffix
+    }
+    const int64_t rereads = prefix_fits ? (int64_t)(num_seqs - 1) * common_prefix_len : 0;
+    const int64_t unique = keys - rereads;
+    const double miss = std::min(kRereadMissMax, std::max(0.0, (rereads * per_key - kRereadFree) / kRereadSlope));
+    const double tp = (unique + miss * rereads) * per_key / kBytesPerUs;
+    const double tc = unique * per_key / kBytesPerUs + kCascadeFixedUs;
+    if (t_plain_us) *t_plain_us = tp;
+    if (t_cascade_us) *t_cascade_us = tc;
+    *use_cascade = common_prefix_len >= kMinPrefix && sliding_window == 0 && prefix_fits && tc < tp ? 1 : 0;
+    return ok();
+}
+
 const char* pkv_last_error(void) { return g_err.c_str(); }
 
 int32_t pkv_version(void) { return 100; }

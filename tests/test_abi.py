@@ -216,3 +216,39 @@ def test_product_path_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liboracle" not in text and "pkv_oracle" not in text, f
+
+
+def test_cascade_choice():
+    # the pages' rules: a prefix under 256 tokens or a sliding window: no
+    use, tp, tc = pkv.use_cascade_attention(255, [100000] * 16, 8, 128)
+    assert not use
+    use, _, _ = pkv.use_cascade_attention(32768, [131072] * 4, 8, 128, sliding_window=4096)
+    assert not use
+    # four requests of 131072 keys sharing 32768: the plain form re-reads
+    # 3 x 134 MB of prefix K/V, which the last-level cache serves, so the
+    # cascade only adds its fixed 50 us
+    unique = 4 * 131072 - 3 * 32768
+    use, tp, tc = pkv.use_cascade_attention(32768, [131072] * 4, 8, 128)
+    assert not use
+    assert abs(tp - unique * 4096 / 5.2e6) < 1e-6
+    assert abs(tc - unique * 4096 / 5.2e6 - 50.0) < 1e-6
+    # sharing 98304 (3 x 403 MB re-read): 35% of the re-reads reach HBM, more
+    # than the cascade's fixed cost
+    unique = 4 * 131072 - 3 * 98304
+    use, tp, tc = pkv.use_cascade_attention(98304, [131072] * 4, 8, 128)
+    assert use
+    assert abs(tp - (unique + 0.35 * 3 * 98304) * 4096 / 5.2e6) < 1e-6
+    # sharing 65536 (0.81 GB re-read): a 14% share, not enough
+    use, tp, tc = pkv.use_cascade_attention(65536, [131072] * 4, 8, 128)
+    assert not use
+    miss = (3 * 65536 * 4096 - 0.55e9) / 1.8e9
+    assert abs(tp - (4 * 131072 - 3 * 65536 + miss * 3 * 65536) * 4096 / 5.2e6) < 1e-6
+    # a short shared prefix saves too little
+    use, tp, tc = pkv.use_cascade_attention(512, [4096] * 8, 8, 128)
+    assert not use and tc > tp
+    # every request must keep at least one token of its own
+    use, _, _ = pkv.use_cascade_attention(4096, [4096, 8192], 8, 128)
+    assert not use
+    # invalid queries
+    with pytest.raises(RuntimeError):
+        pkv.use_cascade_attention(-1, [10], 8, 128)
