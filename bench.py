@@ -41,7 +41,7 @@ FP8_PEAK_TFLOPS = 5000.0
 # fp8-q prefill: Q K^T on the fp8 matrix cores, P V on the bf16 ones, equal
 # flops each, so the time at peak is F/2 / 5.0 + F/2 / 2.5 PFLOP/s
 FP8_QK_BF16_PV_PEAK_TFLOPS = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
-PREFILL_WORKLOADS = ("chunked_prefill", "fp8kv_prefill", "fp8_prefill")
+PREFILL_WORKLOADS = ("chunked_prefill", "fp8kv_prefill", "fp8_prefill", "encoder")
 
 # HBM bytes per launch of the dominant kernel, measured with rocprofv3 counters
 # (FETCH_SIZE, WRITE_SIZE) and scaled by the same counters' reading for a plain
@@ -52,7 +52,7 @@ KERNEL_SOURCES = ["pkv_attn.hip", "pkv_device.h", "pkv_kernels.h"]
 DOMINANT_KERNEL = {"paged_decode": "decode_balanced_kernel", "chunked_prefill": "prefill_kernel",
                    "long_decode": "decode_balanced_kernel", "long_decode_cascade": "decode_balanced_kernel",
                    "fp8_decode": "decode_balanced_kernel", "spec_decode": "prefill_kernel",
-                   "fp8kv_prefill": "prefill_kernel", "fp8_prefill": "prefill_kernel"}
+                   "fp8kv_prefill": "prefill_kernel", "fp8_prefill": "prefill_kernel", "encoder": "prefill_kernel"}
 
 WORKLOADS = {
     "paged_decode": "paged decode, 32/8 heads GQA, head 128, bf16, batch 64, ctx U[512,4096], page 16",
@@ -66,6 +66,8 @@ WORKLOADS = {
                    "32/8 heads, head 128, bf16, page 16",
     "fp8kv_prefill": "chunked prefill over an fp8 e4m3fn cache, bf16 q, batch 8, new U[128,2048] on cached "
                      "U[0,4096], 32/8 heads, head 128, page 16, causal",
+    "encoder": "non-causal encoder attention, flat K/V (no cache), batch 16, lengths U[512,4096], 32 heads MHA, "
+               "head 128, bf16",
     "fp8_prefill": "chunked prefill, fp8 e4m3fn q and cache (QK^T on fp8 MFMA, PV on bf16 MFMA), batch 8, new "
                    "U[128,2048] on cached U[0,4096], 32/8 heads, head 128, page 16, causal",
 }
@@ -89,6 +91,8 @@ def make(name, bs, over=None):
         return workloads.fp8_decode(bs=bs or 16)
     if name == "spec_decode":
         return workloads.spec_decode(bs=bs or 16)
+    if name == "encoder":
+        return workloads.encoder()
     if name == "fp8kv_prefill":
         return workloads.chunked_prefill(bs=bs or 16, cache_dtype="fp8")
     if name == "fp8_prefill":
@@ -326,29 +330,37 @@ def main():
     # device inputs
     q = to_dev(prob.q)
     qsl = to_dev(prob.query_start_loc)
-    seq_lens = to_dev(prob.seq_lens)
-    bt = to_dev(prob.block_table)
+    seq_lens = to_dev(prob.seq_lens) if prob.paged else None
+    bt = to_dev(prob.block_table) if prob.paged else None
     ks = vs = None
     if prob.cache_dtype == "fp8":
         ks = torch.tensor([prob.k_scale], dtype=torch.float32, device=dev)
         vs = torch.tensor([prob.v_scale], dtype=torch.float32, device=dev)
     qs = torch.tensor([prob.q_scale], dtype=torch.float32, device=dev) if prob.q_dtype == "fp8" else None
-    new_rows = prob.new_rows
-    k_new, v_new, slots_new = to_dev(prob.kv_src_k[new_rows]), to_dev(prob.kv_src_v[new_rows]), \
-        to_dev(prob.kv_slots[new_rows])
-    cache_bytes = 2 * prob.num_blocks * prob.bs * prob.Hkv * prob.hd * kv_elem_bytes(prob)
-    R = args.replicas or max(1, min(8, int(np.ceil(1.5e9 / cache_bytes)) + 1))
-    ctx_rows = prob.context_rows()
     reps = []
-    kc0, vc0 = prob.empty_cache()
-    for _ in range(R):
-        kc, vc = to_dev(kc0), to_dev(vc0)
-        for c0 in range(0, len(ctx_rows), 1 << 20):
-            rr = ctx_rows[c0:c0 + (1 << 20)]
-            pkv.pkv_cache_write(to_dev(prob.kv_src_k[rr]), to_dev(prob.kv_src_v[rr]), kc, vc,
-                                to_dev(prob.kv_slots[rr]), ks, vs)
-        reps.append((kc, vc))
-    del kc0, vc0
+    if prob.paged:
+        new_rows = prob.new_rows
+        k_new, v_new, slots_new = to_dev(prob.kv_src_k[new_rows]), to_dev(prob.kv_src_v[new_rows]), \
+            to_dev(prob.kv_slots[new_rows])
+        cache_bytes = 2 * prob.num_blocks * prob.bs * prob.Hkv * prob.hd * kv_elem_bytes(prob)
+        R = args.replicas or max(1, min(8, int(np.ceil(1.5e9 / cache_bytes)) + 1))
+        ctx_rows = prob.context_rows()
+        kc0, vc0 = prob.empty_cache()
+        for _ in range(R):
+            kc, vc = to_dev(kc0), to_dev(vc0)
+            for c0 in range(0, len(ctx_rows), 1 << 20):
+                rr = ctx_rows[c0:c0 + (1 << 20)]
+                pkv.pkv_cache_write(to_dev(prob.kv_src_k[rr]), to_dev(prob.kv_src_v[rr]), kc, vc,
+                                    to_dev(prob.kv_slots[rr]), ks, vs)
+            reps.append((kc, vc))
+        del kc0, vc0
+    else:
+        # flat K/V packed like q: the step is the forward alone (no cache write)
+        flat = np.concatenate(prob.pos_rows)
+        cache_bytes = 2 * len(flat) * prob.Hkv * prob.hd * kv_elem_bytes(prob)
+        R = args.replicas or max(1, min(8, int(np.ceil(1.5e9 / cache_bytes)) + 1))
+        for _ in range(R):
+            reps.append((to_dev(prob.kv_src_k[flat]), to_dev(prob.kv_src_v[flat])))
     torch.cuda.synchronize()
     log(f"[bench] {R} cache replicas of {cache_bytes / 1e9:.3f} GB resident")
 
@@ -370,7 +382,8 @@ def main():
 
     def step(i):
         kc, vc = reps[i % R]
-        pkv.pkv_cache_write(k_new, v_new, kc, vc, slots_new, ks, vs)
+        if prob.paged:
+            pkv.pkv_cache_write(k_new, v_new, kc, vc, slots_new, ks, vs)
         if cascade:
             pkv.cascade_attention(q, kc, vc, qsl, seq_lens, bt, prob.shared_prefix, prob.max_seqlen_q,
                                   prob.max_seqlen_k, prob.scale, k_scale=ks, v_scale=vs, out=out)
@@ -433,7 +446,7 @@ def main():
     else:
         fl = visible_flops(prob, W)
         value = fl / (ms_step * 1e-3) / 1e12
-        metric, unit = "causal prefill TFLOP/s", "TFLOP/s"
+        metric, unit = ("causal prefill TFLOP/s" if prob.causal else "non-causal attention TFLOP/s"), "TFLOP/s"
         achieved = fl / (main_ms / args.steps * 1e-3) / 1e12
         peak = FP8_QK_BF16_PV_PEAK_TFLOPS if prob.q_dtype == "fp8" else BF16_PEAK_TFLOPS
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": "TFLOP/s",
@@ -449,12 +462,17 @@ def main():
         import oracle
         rng = np.random.default_rng(0)
         sample = np.sort(rng.choice(prob.T, size=min(prob.T, 8), replace=False))
-        kc_o, vc_o = prob.empty_cache()
-        kc_o, vc_o = oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc_o, vc_o, prob.kv_slots, prob.bs,
-                                        k_scale=prob.k_scale, v_scale=prob.v_scale)
+        if prob.paged:
+            kc_o, vc_o = prob.empty_cache()
+            kc_o, vc_o = oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc_o, vc_o, prob.kv_slots, prob.bs,
+                                            k_scale=prob.k_scale, v_scale=prob.v_scale)
+            sl_o, bt_o = prob.seq_lens, prob.block_table
+        else:
+            flat = np.concatenate(prob.pos_rows)
+            kc_o, vc_o, sl_o, bt_o = prob.kv_src_k[flat], prob.kv_src_v[flat], None, None
         var_o = dict(window_left=W - 1 if W > 0 else -1, softcap=args.softcap,
                      sinks=None if sinks_h is None else sinks_h.astype(np.float64))
-        ref, ref_lse = oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, prob.seq_lens, prob.block_table,
+        ref, ref_lse = oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, sl_o, bt_o,
                                         scale=prob.scale, causal=prob.causal, rows=sample, k_scale=prob.k_scale,
                                         v_scale=prob.v_scale, q_scale=prob.q_scale, **var_o)
         tol = 5e-2 if prob.cache_dtype == "fp8" else 1e-2
@@ -477,7 +495,7 @@ def main():
         for r0 in range(0, prob.T, 16):
             rows = np.arange(r0, min(prob.T, r0 + 16))
             t1 = time.perf_counter()
-            oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, prob.seq_lens, prob.block_table,
+            oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, sl_o, bt_o,
                              scale=prob.scale, causal=prob.causal, rows=rows, k_scale=prob.k_scale,
                              v_scale=prob.v_scale, nthreads=nthr, q_scale=prob.q_scale, **var_o)
             t_cpu += time.perf_counter() - t1
@@ -507,7 +525,7 @@ def main():
     if args.sinks:
         desc += ", sinks"
     cfg = {"workload": desc, "global_batch": prob.B, "seq_len": prob.max_seqlen_k,
-           "num_heads": prob.H, "num_kv_heads": prob.Hkv, "head_size": prob.hd, "block_size": prob.bs,
+           "num_heads": prob.H, "num_kv_heads": prob.Hkv, "head_size": prob.hd, "block_size": prob.bs if prob.paged else None,
            "kv_cache_dtype": prob.cache_dtype, "num_splits": splits, "cache_replicas": R,
            "launch": "hip_graph" if use_graph else "eager", "ms_per_step_eager": round(ms_eager, 5),
            "parallelism": "single GPU"}

@@ -12,6 +12,7 @@ Workloads (seeded, synthetic; the recipes are in workloads/):
   * chunked prefill: batch 8, new U[128, 2048] on cached U[0, 4096], 32/8 heads, page 16
   * long decode: batch 4, context 131072, 64/8 heads, page 256 (plain, and as
     a cascade over a 32768-token prefix shared by all four requests)
+  * encoder: 16 requests of U[512, 4096] tokens, non-causal, flat K/V, 32 heads MHA
   * fp8 e4m3fn decode: batch 128, context U[1024, 8192], 32/8 heads, swept
     over page sizes 1, 8, 16, 64 and 256 (the same logical K/V each time)
 """
@@ -87,6 +88,18 @@ def test_full_long_decode_cascade():
     rows = np.arange(prob.T)
     ref, ref_lse = oracle_attention(prob, rows=rows)
     assert_parity(out, lse, ref, ref_lse, BF16_OUT, BF16_LSE, rows=rows, what="long decode cascade")
+
+
+def test_full_encoder():
+    """Non-causal attention over flat K/V: 16 requests of U[512, 4096] tokens, 32 heads MHA."""
+    prob = workloads.encoder()
+    g = GpuProblem(prob)
+    out, lse = g.run(num_splits=0)
+    torch.cuda.synchronize()
+    check_whole_output(prob, out, lse)
+    rows = sample_rows(prob, 24, 4)
+    ref, ref_lse = oracle_attention(prob, rows=rows)
+    assert_parity(out, lse, ref, ref_lse, BF16_OUT, BF16_LSE, rows=rows, what="encoder")
 
 
 @pytest.fixture(scope="module")

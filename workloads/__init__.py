@@ -287,6 +287,15 @@ def spec_decode(seed: int = 6, B: int = 64, qlo: int = 2, qhi: int = 16, lo: int
     return make_problem(seed * 1000 + 1, ql, ctx, H=H, Hkv=Hkv, hd=hd, bs=bs)
 
 
+def encoder(seed: int = 7, B: int = 16, lo: int = 512, hi: int = 4096, H: int = 32, Hkv: int = 32,
+            hd: int = 128) -> Problem:
+    """Non-causal (encoder) attention over flat K/V packed like q: lengths
+    uniform in [lo, hi], no cache."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    return make_problem(seed * 1000 + 1, L, np.zeros(B, np.int32), H=H, Hkv=Hkv, hd=hd, causal=False, paged=False)
+
+
 def chunked_prefill(seed: int = 3, B: int = 8, qlo: int = 128, qhi: int = 2048, clo: int = 0, chi: int = 4096,
                     H: int = 32, Hkv: int = 8, hd: int = 128, bs: int = 16, q_dtype: str = "bf16",
                     cache_dtype: str = "bf16") -> Problem:
