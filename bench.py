@@ -406,7 +406,8 @@ def main():
         step(args.warmup + i)
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t_start) * 1e3 / args.steps
-    calls, main_ms, merge_ms = pkv.timing_collect()
+    main_each, merge_each = pkv.timing_collect_calls()
+    calls, main_ms, merge_ms = len(main_each), float(sum(main_each)), float(sum(merge_each))
     pkv.timing_enable(False)
 
     use_graph = not args.eager
@@ -440,9 +441,15 @@ def main():
         # the dominant kernel is the attention kernel; per step it reads the
         # whole KV once (cascade: a prefix launch and a suffix launch per step)
         achieved = kvb / (main_ms / args.steps * 1e-3) / 1e9
+        # every algorithmic byte: K/V, q, out, lse and the block-table entries read
+        used_pages = int(((prob.seq_lens.astype(np.int64) + prob.bs - 1) // prob.bs).sum()) if prob.paged else 0
+        all_bytes = kvb + prob.T * prob.H * prob.hd * 2 * (1 if prob.q_dtype == "fp8" else 2) \
+            + prob.T * prob.H * prob.hd * 2 + prob.T * prob.H * 4 + used_pages * 4
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "algorithmic_bytes_per_launch": kvb}
+                    "algorithmic_bytes_per_launch": kvb,
+                    "all_algorithmic_bytes_per_launch": int(all_bytes),
+                    "achieved_all_bytes": round(all_bytes / (main_ms / args.steps * 1e-3) / 1e9, 1)}
     else:
         fl = visible_flops(prob, W)
         value = fl / (ms_step * 1e-3) / 1e12
@@ -524,6 +531,9 @@ def main():
         desc += f", softcap {args.softcap:g}"
     if args.sinks:
         desc += ", sinks"
+    med = float(np.median(main_each)) if main_each else None
+    roofline["kernel_ms_median"] = round(med, 5) if med else None
+    roofline["kernel_ms_min"] = round(float(min(main_each)), 5) if main_each else None
     cfg = {"workload": desc, "global_batch": prob.B, "seq_len": prob.max_seqlen_k,
            "num_heads": prob.H, "num_kv_heads": prob.Hkv, "head_size": prob.hd, "block_size": prob.bs if prob.paged else None,
            "kv_cache_dtype": prob.cache_dtype, "num_splits": splits, "cache_replicas": R,

@@ -247,9 +247,12 @@ int32_t pkv_version(void);
  * pkv_timing_collect waits for the recorded events, returns the number of
  * calls and the summed milliseconds of each kernel, and clears the record.
  * Enabling creates the events (it is the only call that allocates); disabling
- * releases them. Not thread-safe.                                            */
+ * releases them. Not thread-safe. pkv_timing_collect_calls does the same but
+ * writes each call's milliseconds (main kernel, merge kernel or 0) to the
+ * host arrays main_ms / merge_ms, at most cap entries, in call order.       */
 pkv_status pkv_timing_enable(int32_t on);
 pkv_status pkv_timing_collect(int32_t* calls, double* main_ms, double* merge_ms);
+pkv_status pkv_timing_collect_calls(int32_t* calls, float* main_ms, float* merge_ms, int32_t cap);
 
 #ifdef __cplusplus
 }

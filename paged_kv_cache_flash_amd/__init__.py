@@ -70,7 +70,7 @@ class pkv_varlen_args(ctypes.Structure):
 EXPORTS = ("pkv_cache_write", "pkv_varlen_args_size", "pkv_varlen_check", "pkv_varlen_num_splits",
            "pkv_varlen_workspace_size", "pkv_varlen_fwd", "pkv_merge_attn_states", "pkv_cascade_choose",
            "pkv_last_error",
-           "pkv_version", "pkv_timing_enable", "pkv_timing_collect")
+           "pkv_version", "pkv_timing_enable", "pkv_timing_collect", "pkv_timing_collect_calls")
 
 _lib = None
 
@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_timing_collect.restype = i32
     L.pkv_timing_collect.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_double)]
+    L.pkv_timing_collect_calls.restype = i32
+    L.pkv_timing_collect_calls.argtypes = [ctypes.POINTER(i32), vp, vp, i32]
     if L.pkv_varlen_args_size() != ctypes.sizeof(pkv_varlen_args):
         raise RuntimeError("pkv_varlen_args layout mismatch between the library and the binding")
     _lib = L
@@ -312,6 +314,18 @@ def cascade_attention(q, k_cache, v_cache, query_start_loc, seq_lens, block_tabl
 
 def timing_enable(on: bool = True):
     _check(lib().pkv_timing_enable(1 if on else 0))
+
+
+def timing_collect_calls(cap=4096):
+    """Per-call milliseconds since the last collect: (main kernel list, merge kernel list)."""
+    import numpy as np
+    a = np.zeros(cap, np.float32)
+    b = np.zeros(cap, np.float32)
+    c = ctypes.c_int32()
+    _check(lib().pkv_timing_collect_calls(ctypes.byref(c), a.ctypes.data_as(ctypes.c_void_p),
+                                          b.ctypes.data_as(ctypes.c_void_p), int(cap)))
+    n = min(c.value, cap)
+    return a[:n].tolist(), b[:n].tolist()
 
 
 def timing_collect():

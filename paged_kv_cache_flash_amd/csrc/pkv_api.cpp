@@ -434,26 +434,45 @@ pkv_status pkv_timing_enable(int32_t on) {
     return ok();
 }
 
+// Milliseconds of call i's main kernel and merge kernel (0 without one).
+static pkv_status timing_of(int i, float& main_ms, float& merge_ms) {
+    hipError_t e = hipEventSynchronize(g_tim.ev[4 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    e = hipEventElapsedTime(&main_ms, g_tim.ev[4 * i], g_tim.ev[4 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    merge_ms = 0.f;
+    if (g_tim.has_merge[i]) {
+        e = hipEventSynchronize(g_tim.ev[4 * i + 3]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        e = hipEventElapsedTime(&merge_ms, g_tim.ev[4 * i + 2], g_tim.ev[4 * i + 3]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    }
+    return ok();
+}
+
 pkv_status pkv_timing_collect(int32_t* calls, double* main_ms, double* merge_ms) {
     double a = 0, b = 0;
     for (int i = 0; i < g_tim.calls; ++i) {
-        hipError_t e = hipEventSynchronize(g_tim.ev[4 * i + 1]);
-        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-        float ms = 0;
-        e = hipEventElapsedTime(&ms, g_tim.ev[4 * i], g_tim.ev[4 * i + 1]);
-        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-        a += ms;
-        if (g_tim.has_merge[i]) {
-            e = hipEventSynchronize(g_tim.ev[4 * i + 3]);
-            if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-            e = hipEventElapsedTime(&ms, g_tim.ev[4 * i + 2], g_tim.ev[4 * i + 3]);
-            if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-            b += ms;
-        }
+        float m = 0.f, g = 0.f;
+        pkv_status st = timing_of(i, m, g);
+        if (st != PKV_OK) return st;
+        a += m;
+        b += g;
     }
     if (calls) *calls = g_tim.calls;
     if (main_ms) *main_ms = a;
     if (merge_ms) *merge_ms = b;
+    g_tim.calls = 0;
+    return ok();
+}
+
+pkv_status pkv_timing_collect_calls(int32_t* calls, float* main_ms, float* merge_ms, int32_t cap) {
+    if (cap < 0 || (cap > 0 && (!main_ms || !merge_ms))) return fail(PKV_ERR_INVALID_ARG, "invalid timing buffers");
+    for (int i = 0; i < g_tim.calls && i < cap; ++i) {
+        pkv_status st = timing_of(i, main_ms[i], merge_ms[i]);
+        if (st != PKV_OK) return st;
+    }
+    if (calls) *calls = g_tim.calls;
     g_tim.calls = 0;
     return ok();
 }
