@@ -70,7 +70,7 @@ def lib():
         L.or_attention.restype = i32
         L.or_attention.argtypes = common + [vp, i64, vp, vp, i32]
         L.or_attention_ex.restype = i32
-        L.or_attention_ex.argtypes = common + [i64, dbl, vp, vp, i64, vp, vp, i32]
+        L.or_attention_ex.argtypes = common + [i64, dbl, vp, vp, vp, i64, vp, vp, i32]
         for nm in ("or_attention_online", "or_attention_online_normalised"):
             getattr(L, nm).restype = i32
             getattr(L, nm).argtypes = common + [i32, vp, vp]
@@ -126,7 +126,7 @@ def _prep(q, k, v, query_start_loc, seq_lens, block_table, H, Hkv, bs):
 
 def attention(q, k, v, query_start_loc, seq_lens=None, block_table=None, *, scale, causal=True,
               k_scale=1.0, v_scale=1.0, rows=None, nthreads=0, window_left=-1, softcap=0.0, sinks=None,
-              q_scale=1.0):
+              q_scale=1.0, alibi=None):
     """Definition of the varlen (optionally paged) attention forward.
 
     Returns (out [n_rows, H, hd] float64, lse [H, n_rows] float64). ``rows``
@@ -134,7 +134,8 @@ def attention(q, k, v, query_start_loc, seq_lens=None, block_table=None, *, scal
     Variants: ``window_left`` >= 0 limits query position i to keys
     j >= i - window_left; ``softcap`` > 0 maps each scaled score s to
     softcap * tanh(s / softcap); ``sinks`` [H] adds one logit per head to the
-    softmax normaliser (no value row). An e4m3fn q (uint8 codes) stands for
+    softmax normaliser (no value row); ``alibi`` [H] slopes add -slope * |i - j|
+    to the score of query position i and key j (after the cap). An e4m3fn q (uint8 codes) stands for
     its decoded values times ``q_scale``; the factor is applied to the scale
     (each score is linear in q)."""
     q, k, v, qsl, seq_lens, bt, bt_stride, B, T, H, Hkv, hd, bs = _prep(q, k, v, query_start_loc, seq_lens,
@@ -148,10 +149,11 @@ def attention(q, k, v, query_start_loc, seq_lens=None, block_table=None, *, scal
     out = np.zeros((n, H, hd), np.float64)
     lse = np.zeros((H, n), np.float64)
     sk = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float64).reshape(H)
+    al = None if alibi is None else np.ascontiguousarray(alibi, dtype=np.float64).reshape(H)
     rc = lib().or_attention_ex(_ptr(q), _code(q), _ptr(k), _ptr(v), _code(k), float(k_scale), float(v_scale),
                                _ptr(qsl), _ptr(seq_lens), _ptr(bt), bt_stride, B, H, Hkv, hd, bs,
                                float(scale) * float(q_scale), int(bool(causal)), int(window_left), float(softcap),
-                               _ptr(sk),
+                               _ptr(sk), _ptr(al),
                                _ptr(rows_arr), n, _ptr(out), _ptr(lse), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the problem (H % Hkv != 0 or empty batch)")

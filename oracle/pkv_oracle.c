@@ -215,6 +215,7 @@ typedef struct {
     int64_t window_left;  /* < 0: no window */
     double softcap;       /* <= 0: no cap */
     const double* sinks;  /* [H] or NULL */
+    const double* alibi;  /* [H] ALiBi slopes or NULL */
 } or_problem;
 
 static int request_of(const or_problem* p, int64_t tok) {
@@ -265,6 +266,8 @@ static void attend_one(const or_problem* p, int64_t tok, int h, double* s, doubl
     int g = h / (p->H / p->Hkv);
     int64_t n = visible(p, r, t);
     int64_t lo = first_visible(p, r, t);
+    int64_t q_len = p->qsl[r + 1] - p->qsl[r];
+    int64_t i_pos = (p->block_table ? p->seq_lens[r] : q_len) - q_len + t;  /* the query's position */
     int hd = p->hd;
     double sink = p->sinks ? p->sinks[h] : -INFINITY;
     for (int d = 0; d < hd; ++d) qv[d] = load_elem(p->q, p->q_dtype, (tok * p->H + h) * hd + d);
@@ -277,6 +280,7 @@ static void attend_one(const or_problem* p, int64_t tok, int h, double* s, doubl
         for (int d = 0; d < hd; ++d) dot += qv[d] * (load_elem(p->k, p->kv_dtype, off + d) * p->k_scale);
         s[j] = p->scale * dot;
         if (p->softcap > 0) s[j] = p->softcap * tanh(s[j] / p->softcap);
+        if (p->alibi) s[j] -= p->alibi[h] * fabs((double)(i_pos - j));
         if (s[j] > m) m = s[j];
     }
     /* the sink is one more logit in the normaliser; it adds no value row */
@@ -312,15 +316,18 @@ static int64_t max_len(const or_problem* p) {
  *                    joins the softmax normaliser and contributes no value:
  *                    out = sum_j e^{s_j} v_j / (e^{sink} + sum_j e^{s_j}),
  *                    lse = log(e^{sink} + sum_j e^{s_j}); a row with no
- *                    visible key then has out = 0 and lse = sink. */
+ *                    visible key then has out = 0 and lse = sink;
+ *  alibi != NULL:    ALiBi -- the score of query position i and key j
+ *                    (after the cap) gets -alibi[h] * |i - j| added. */
 int or_attention_ex(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
                     double k_scale, double v_scale, const int32_t* qsl, const int32_t* seq_lens,
                     const int32_t* block_table, int64_t bt_stride, int B, int H, int Hkv, int hd, int bs,
                     double scale, int causal, int64_t window_left, double softcap, const double* sinks,
-                    const int64_t* rows, int64_t n_rows, double* out, double* lse, int nthreads) {
+                    const double* alibi, const int64_t* rows, int64_t n_rows, double* out, double* lse,
+                    int nthreads) {
     if (H % Hkv != 0 || B <= 0) return -1;
     or_problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, qsl, seq_lens, block_table,
-                    bt_stride, B, H, Hkv, hd, bs, scale, causal, window_left, softcap, sinks};
+                    bt_stride, B, H, Hkv, hd, bs, scale, causal, window_left, softcap, sinks, alibi};
     int64_t L = max_len(&p);
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -352,7 +359,8 @@ int or_attention(const void* q, int q_dtype, const void* k, const void* v, int k
                  double scale, int causal, const int64_t* rows, int64_t n_rows,
                  double* out, double* lse, int nthreads) {
     return or_attention_ex(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, qsl, seq_lens, block_table, bt_stride,
-                           B, H, Hkv, hd, bs, scale, causal, -1, 0.0, NULL, rows, n_rows, out, lse, nthreads);
+                           B, H, Hkv, hd, bs, scale, causal, -1, 0.0, NULL, NULL, rows, n_rows, out, lse,
+                           nthreads);
 }
 
 /* Number of threads OpenMP would use (for reporting). */

@@ -18,7 +18,7 @@ def decode(a: np.ndarray, e4m3_table=None) -> np.ndarray:
 
 
 def global_attention(q, k_flat, v_flat, q_start, kv_start, *, scale, causal, H, Hkv, window_left=-1,
-                     softcap=0.0, sinks=None):
+                     softcap=0.0, sinks=None, alibi=None):
     """q: [T, H, hd]; k_flat/v_flat: [sum L, Hkv, hd] packed per request in
     position order; q_start [B+1], kv_start [B+1]. Returns out [T, H, hd],
     lse [H, T] (natural log).
@@ -26,17 +26,23 @@ def global_attention(q, k_flat, v_flat, q_start, kv_start, *, scale, causal, H, 
     Variants: a window keeps, for the query at sequence position i, only keys
     at positions >= i - window_left; a soft cap maps scores through
     softcap * tanh(s / softcap); a sink is one more column of the global
-    matrix, visible to every query of its head, with a zero value row."""
+    matrix, visible to every query of its head, with a zero value row; ALiBi
+    subtracts slope[h] * |i - j| (sequence positions of query and key) from
+    the (capped) score."""
     qd, kd, vd = decode(q), decode(k_flat), decode(v_flat)
     T = qd.shape[0]
     N = kd.shape[0]
     B = len(q_start) - 1
     allowed = np.zeros((T, N), bool)
+    qpos = np.zeros(T)   # each packed query's and key's position in its own sequence
+    kpos = np.zeros(N)
     for r in range(B):
         q0, q1 = q_start[r], q_start[r + 1]
         k0, k1 = kv_start[r], kv_start[r + 1]
         qn, L = q1 - q0, k1 - k0
         ctx = L - qn
+        qpos[q0:q1] = ctx + np.arange(qn)
+        kpos[k0:k1] = np.arange(L)
         for t in range(qn):
             n = (ctx + t + 1) if causal else L
             n = max(0, min(n, L))
@@ -51,6 +57,8 @@ def global_attention(q, k_flat, v_flat, q_start, kv_start, *, scale, causal, H, 
         S = scale * (qd[:, h, :] @ kd[:, h // g, :].T)          # [T, N] global matrix
         if softcap > 0:
             S = softcap * np.tanh(S / softcap)
+        if alibi is not None:
+            S = S - float(alibi[h]) * np.abs(qpos[:, None] - kpos[None, :])
         S = np.where(allowed, S, -np.inf)
         Vh = vd[:, h // g, :]
         if sinks is not None:                                    # the sink column and its zero value row

@@ -505,7 +505,14 @@ VARIANT_CASES = [
     dict(window_left=-1, softcap=2.0, sinks=False),
     dict(window_left=-1, softcap=0.0, sinks=True),
     dict(window_left=5, softcap=1.5, sinks=True),
+    dict(window_left=-1, softcap=0.0, sinks=False, alibi=True),
+    dict(window_left=4, softcap=1.5, sinks=True, alibi=True),
 ]
+
+
+def _alibi(prob):
+    """The ALiBi paper's geometric slopes 2^(-8 h / H), h = 1 .. H."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / prob.H) for h in range(prob.H)])
 
 
 def _variant_problem(seed=46):
@@ -528,11 +535,13 @@ def _oracle_variant(prob, causal, **kw):
 def test_variants_match_global_matrix_brute_force(var, causal):
     prob = _variant_problem()
     sinks = _sinks(prob) if var["sinks"] else None
-    out, lse = _oracle_variant(prob, causal, window_left=var["window_left"], softcap=var["softcap"], sinks=sinks)
+    alibi = _alibi(prob) if var.get("alibi") else None
+    out, lse = _oracle_variant(prob, causal, window_left=var["window_left"], softcap=var["softcap"], sinks=sinks,
+                               alibi=alibi)
     kf, vf, loc = prob.flat_kv()
     b_out, b_lse = global_attention(prob.q, kf, vf, prob.query_start_loc, loc, scale=prob.scale, causal=causal,
                                     H=prob.H, Hkv=prob.Hkv, window_left=var["window_left"], softcap=var["softcap"],
-                                    sinks=sinks)
+                                    sinks=sinks, alibi=alibi)
     np.testing.assert_allclose(out, b_out, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, b_lse, rtol=0, atol=1e-12)
 
@@ -646,3 +655,23 @@ def test_fp8_q_equals_decoded_q_times_scale():
                                     Hkv=prob.Hkv)
     np.testing.assert_allclose(a[0], b_out, rtol=0, atol=1e-6)
     np.testing.assert_allclose(a[1], b_lse, rtol=0, atol=1e-6)
+
+
+def test_alibi_closed_forms():
+    """Zero slopes change nothing; slopes so steep that every key but the
+    query's own one is worth e^-50 or less leave the query's own V row (causal:
+    the nearest key is the query itself), with lse its own score."""
+    prob = _variant_problem(54)
+    a = _oracle_variant(prob, True)
+    z = _oracle_variant(prob, True, alibi=np.zeros(prob.H))
+    assert np.array_equal(a[0], z[0]) and np.array_equal(a[1], z[1])
+    out, lse = _oracle_variant(prob, True, alibi=np.full(prob.H, 100.0))
+    q = workloads.storage_to_f32(prob.q).astype(np.float64)
+    k = workloads.storage_to_f32(prob.kv_src_k).astype(np.float64)
+    v = workloads.storage_to_f32(prob.kv_src_v).astype(np.float64)
+    g = prob.H // prob.Hkv
+    for tok in range(prob.T):
+        row = prob.new_rows[tok]
+        for h in range(prob.H):
+            np.testing.assert_allclose(out[tok, h], v[row, h // g], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[h, tok], prob.scale * q[tok, h] @ k[row, h // g], rtol=0, atol=1e-12)

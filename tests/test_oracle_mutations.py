@@ -37,6 +37,8 @@ MUTANTS = {
                            "int64_t lo = (L - q_len) + t - p->window_left + 1;")],
     "softcap_no_division": [("s[j] = p->softcap * tanh(s[j] / p->softcap);", "s[j] = p->softcap * tanh(s[j]);")],
     "sink_dropped": [("double z = sink == -INFINITY ? 0.0 : exp(sink - m);", "double z = 0.0;")],
+    "alibi_local_index": [("int64_t i_pos = (p->block_table ? p->seq_lens[r] : q_len) - q_len + t;",
+                           "int64_t i_pos = t;")],
 }
 
 
