@@ -16,7 +16,7 @@ Other workloads (--workload): chunked_prefill (TFLOP/s against the 2.5 PFLOP/s
 bf16 dense MFMA peak), long_decode, long_decode_cascade, fp8_decode,
 spec_decode (several new tokens per request; KV GB/s). The
 attention variants can be switched on for any workload but the cascade
-(--sliding-window W, --softcap C, --sinks); bytes and flops then count only
+(--sliding-window W, --softcap C, --sinks, --alibi); bytes and flops then count only
 what the window leaves visible.
 
 Prints ONE JSON line. The float64 CPU oracle is timed on the same workload
@@ -267,6 +267,7 @@ def main():
     ap.add_argument("--sliding-window", type=int, default=0, help="a query sees at most this many keys (0: off)")
     ap.add_argument("--softcap", type=float, default=0.0, help="logits soft cap (0: off)")
     ap.add_argument("--sinks", action="store_true", help="one sink logit per query head (seeded)")
+    ap.add_argument("--alibi", action="store_true", help="ALiBi with the geometric slopes 2^(-8 (h + 1) / H)")
     ap.add_argument("--replicas", type=int, default=0, help="KV cache copies used in turn (0 = enough for 1.5 GB)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: the timed steps are one captured HIP graph)")
@@ -317,7 +318,7 @@ def main():
         if a.dtype == np.uint8:
             return torch.from_numpy(a).to(dev).view(torch.float8_e4m3fn)
         return torch.from_numpy(a).to(dev)
-    variants = args.sliding_window > 0 or args.softcap > 0 or args.sinks
+    variants = args.sliding_window > 0 or args.softcap > 0 or args.sinks or args.alibi
     if variants and args.workload == "long_decode_cascade":
         raise SystemExit("bench: the attention variants are not benchmarked on the cascade workload")
     t0 = time.time()
@@ -369,8 +370,10 @@ def main():
     cascade = prob.shared_prefix > 0
     W = args.sliding_window
     sinks_h = np.random.default_rng(12345).normal(1.5, 2.0, prob.H).astype(np.float32) if args.sinks else None
+    alibi_h = (2.0 ** (-8.0 * (np.arange(prob.H) + 1) / prob.H)).astype(np.float32) if args.alibi else None
     fwd_kw = dict(softmax_scale=prob.scale, causal=prob.causal, k_scale=ks, v_scale=vs, sliding_window=W,
-                  softcap=args.softcap, sinks=None if sinks_h is None else to_dev(sinks_h), q_scale=qs)
+                  softcap=args.softcap, sinks=None if sinks_h is None else to_dev(sinks_h), q_scale=qs,
+                  alibi_slopes=None if alibi_h is None else to_dev(alibi_h))
     if not cascade:
         need = pkv.pkv_varlen_workspace_size(q, reps[0][0], reps[0][1], qsl, seq_lens, bt, prob.max_seqlen_q,
                                              prob.max_seqlen_k, prob.scale, prob.causal, args.num_splits, W)
@@ -478,7 +481,8 @@ def main():
             flat = np.concatenate(prob.pos_rows)
             kc_o, vc_o, sl_o, bt_o = prob.kv_src_k[flat], prob.kv_src_v[flat], None, None
         var_o = dict(window_left=W - 1 if W > 0 else -1, softcap=args.softcap,
-                     sinks=None if sinks_h is None else sinks_h.astype(np.float64))
+                     sinks=None if sinks_h is None else sinks_h.astype(np.float64),
+                     alibi=None if alibi_h is None else alibi_h.astype(np.float64))
         ref, ref_lse = oracle.attention(prob.q, kc_o, vc_o, prob.query_start_loc, sl_o, bt_o,
                                         scale=prob.scale, causal=prob.causal, rows=sample, k_scale=prob.k_scale,
                                         v_scale=prob.v_scale, q_scale=prob.q_scale, **var_o)
@@ -531,6 +535,8 @@ def main():
         desc += f", softcap {args.softcap:g}"
     if args.sinks:
         desc += ", sinks"
+    if args.alibi:
+        desc += ", ALiBi"
     med = float(np.median(main_each)) if main_each else None
     roofline["kernel_ms_median"] = round(med, 5) if med else None
     roofline["kernel_ms_min"] = round(float(min(main_each)), 5) if main_each else None

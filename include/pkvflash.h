@@ -98,8 +98,8 @@ pkv_status pkv_cache_write(const void* key, const void* value, pkv_dtype src_dty
  *   lse[h][t] = log(sum_j exp(softmax_scale * q[t][h] . k_j))   (natural log)
  * A row with no visible key gets out = 0 and lse = -inf.
  * Variants (the deep-dive page's table of supported variants names a sliding
- * window, a logits soft cap and attention sinks without formulas; these are
- * the plainest readings, each off by default):
+ * window, a logits soft cap, attention sinks and ALiBi without formulas;
+ * these are the plainest readings, each off by default):
  *   sliding_window > 0: the query at position i = ctx_r + t sees only the
  *          keys j >= i - (sliding_window - 1), at most sliding_window keys
  *          ending at its own position (on top of the causal bound); 0: no
@@ -114,6 +114,11 @@ pkv_status pkv_cache_write(const void* key, const void* value, pkv_dtype src_dty
  *          gets out = 0, lse = sinks[h]. Split partials exclude the sink and
  *          the merge adds it once (a cascade passes sinks to one of its two
  *          forward calls only).
+ *   alibi_slopes != NULL: alibi_slopes[h] (device fp32, [num_heads]) adds the
+ *          linear position bias -alibi_slopes[h] * |i - j| to the score of
+ *          query position i = ctx_r + t and key j, after the soft cap. The
+ *          positions are those of the request's own sequence, so a cascade's
+ *          prefix pass (which sees every query as one request) cannot carry it.
  *
  * Layouts: q, out [num_tokens, num_heads, head_size] in q_dtype (out has the
  *          type of q, except bf16 for an FP8_E4M3FN q); lse [num_heads,
@@ -174,6 +179,7 @@ typedef struct pkv_varlen_args {
     float softcap;          /* 0: no logits soft cap */
     const float* sinks;     /* [num_heads] device fp32, or NULL */
     const float* q_scale;   /* FP8 q only: device fp32 */
+    const float* alibi_slopes; /* [num_heads] device fp32, or NULL */
 } pkv_varlen_args;
 
 /* sizeof(pkv_varlen_args), so bindings can check their mirror of the struct. */

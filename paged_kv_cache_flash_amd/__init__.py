@@ -64,6 +64,7 @@ class pkv_varlen_args(ctypes.Structure):
         ("softcap", ctypes.c_float),
         ("sinks", ctypes.c_void_p),
         ("q_scale", ctypes.c_void_p),
+        ("alibi_slopes", ctypes.c_void_p),
     ]
 
 
@@ -170,10 +171,12 @@ def pkv_cache_write(key, value, k_cache, v_cache, slot_mapping, k_scale=None, v_
 
 def _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
                  softmax_scale, causal, out, lse, k_scale, v_scale, num_splits, workspace, sliding_window=0,
-                 softcap=0.0, sinks=None, q_scale=None):
-    _contig(q, k_cache, v_cache, query_start_loc, seq_lens, out, lse, workspace, sinks)
+                 softcap=0.0, sinks=None, q_scale=None, alibi_slopes=None):
+    _contig(q, k_cache, v_cache, query_start_loc, seq_lens, out, lse, workspace, sinks, alibi_slopes)
     if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != q.shape[1]):
         raise ValueError("sinks must be a float32 tensor of num_heads elements")
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != q.shape[1]):
+        raise ValueError("alibi_slopes must be a float32 tensor of num_heads elements")
     T, H, hd = q.shape
     a = pkv_varlen_args()
     a.q, a.k_cache, a.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
@@ -206,6 +209,7 @@ def _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, ma
     a.softcap = float(softcap)
     a.sinks = _ptr(sinks)
     a.q_scale = _ptr(q_scale)
+    a.alibi_slopes = _ptr(alibi_slopes)
     return a
 
 
@@ -231,12 +235,13 @@ def pkv_varlen_num_splits(q, k_cache, v_cache, query_start_loc, seq_lens, block_
 def pkv_varlen_fwd(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
                    softmax_scale, causal=True, out=None, lse=None, k_scale=None, v_scale=None, num_splits=0,
                    workspace=None, return_lse=False, stream=None, sliding_window=0, softcap=0.0, sinks=None,
-                   q_scale=None):
+                   q_scale=None, alibi_slopes=None):
     """Varlen attention forward. q [T, H, hd]; paged caches [num_blocks, bs, Hkv, hd] with block_table
     [B, >= ceil(max_seqlen_k / bs)] int32 (a column slice of a larger table is fine), or flat caches
     [T, Hkv, hd] with block_table None. Returns out (and lse [H, T] fp32 when requested).
     Variants: sliding_window (a query sees at most this many keys, ending at its own position; 0: none),
-    softcap (0: none), sinks (float32 [H] on the device, or None). An e4m3fn q (with a float32 q_scale
+    softcap (0: none), sinks (float32 [H] on the device, or None), alibi_slopes (float32 [H] on the
+    device, or None: the score of query position i and key j gets -slope * |i - j|). An e4m3fn q (with a float32 q_scale
     on the device) runs over an e4m3fn cache and gives a bf16 out."""
     T, H, hd = q.shape
     if out is None:
@@ -252,7 +257,7 @@ def pkv_varlen_fwd(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, 
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a = _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
                      softmax_scale, causal, out, lse, k_scale, v_scale, num_splits, workspace, sliding_window, softcap,
-                     sinks, q_scale)
+                     sinks, q_scale, alibi_slopes)
     _check(lib().pkv_varlen_fwd(ctypes.byref(a), _stream(stream)))
     return (out, lse) if return_lse else out
 

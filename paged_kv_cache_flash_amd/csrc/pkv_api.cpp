@@ -283,6 +283,7 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     p.softcap_l2 = a->softcap > 0.f ? a->softcap * 1.4426950408889634f : 0.f;
     p.softcap_inv2 = a->softcap > 0.f ? 2.f / a->softcap : 0.f;
     p.sinks = a->sinks;
+    p.alibi = a->alibi_slopes;
     if (pl.kind == Kind::DecodeBalanced) {
         const int64_t slots = pl.splits + (int64_t)a->num_seqs * a->num_kv_heads;
         p.sk_waves = pl.splits;

@@ -120,6 +120,10 @@ __device__ __forceinline__ float softcap_l2(float x, float cap_l2, float cap_inv
     return cap_l2 * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
 }
 
+// ALiBi slope of query head h in the log2 domain (0 without ALiBi): the
+// score of query position i and key j gets -slope * |i - j| added.
+__device__ __forceinline__ float alibi_l2(const FwdParams& p, int h) { return p.alibi ? p.alibi[h] * kLog2e : 0.f; }
+
 // Sink logit of query head h in the log2 domain (-inf without sinks).
 __device__ __forceinline__ float sink_l2(const FwdParams& p, int h) {
     return p.sinks ? p.sinks[h] * kLog2e : -INFINITY;
@@ -214,14 +218,16 @@ struct DecodeTile {
     }
     // One tile from LDS: S^T with K as the A operand and the item's query
     // rows as the 16 columns, masking keys at or past `limit` (per row) and,
-    // with the variants compiled in (VAR), keys before `lo` and applying the
-    // soft cap (cap_l2 > 0),
+    // with the variants compiled in (VAR), keys before `lo`, applying the
+    // soft cap (cap_l2 > 0) and the ALiBi bias (slope al2, query position
+    // qpos),
     // online softmax, then O^T += V^T P^T with V^T read transposed. m_run is
     // row-uniform (log2 domain), l_run per lane (this lane's keys only).
     template <bool VAR>
     static __device__ __forceinline__ void compute(const uint16_t* stage, int lane, int t0, int lo, int limit,
-                                                   float sl2, float cap_l2, float cap_inv2, const u32x4 (&qf)[KS],
-                                                   float& m_run, float& l_run, f32x4 (&oacc)[MB]) {
+                                                   float sl2, float cap_l2, float cap_inv2, float al2, int qpos,
+                                                   const u32x4 (&qf)[KS], float& m_run, float& l_run,
+                                                   f32x4 (&oacc)[MB]) {
         const uint16_t* const kl = stage;
         const uint16_t* const vl = stage + K_ELEMS;
         const int row = lane & 15;
@@ -245,6 +251,7 @@ struct DecodeTile {
                 float x = sacc[b][i] * sl2;
                 if constexpr (VAR) {
                     if (cap_l2 > 0.f) x = softcap_l2(x, cap_l2, cap_inv2);
+                    if (al2 != 0.f) x -= al2 * fabsf((float)(qpos - key));
                     x = key < limit && key >= lo ? x : -INFINITY;
                 } else {
                     x = key < limit ? x : -INFINITY;
@@ -306,6 +313,14 @@ __device__ __forceinline__ int decode_row_lo(const FwdParams& p, int lane, int q
     return window_lo(p, L - q_len + row / p.g);
 }
 
+// Sequence position and log2-domain ALiBi slope of query row row0 + lane % 16.
+__device__ __forceinline__ int decode_row_pos(const FwdParams& p, int lane, int q_len, int L, int row0 = 0) {
+    return L - q_len + (row0 + (lane & 15)) / p.g;
+}
+__device__ __forceinline__ float decode_row_alibi(const FwdParams& p, int lane, int kh, int row0 = 0) {
+    return alibi_l2(p, kh * p.g + (row0 + (lane & 15)) % p.g);
+}
+
 // Largest key index + 1 that query row row0 + lane % 16 of an item may see.
 __device__ __forceinline__ int decode_row_limit(const FwdParams& p, int lane, int q_len, int L, int row0 = 0) {
     const int row = row0 + (lane & 15);
@@ -330,6 +345,8 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage
     load_decode_q<HD>(p, lane, q0, q_len * p.g, kh, qf);
     const int limit = min(decode_row_limit(p, lane, q_len, L), k_end);
     const int lo = VAR ? decode_row_lo(p, lane, q_len, L) : 0;
+    const float al2 = VAR ? decode_row_alibi(p, lane, kh) : 0.f;
+    const int qpos = decode_row_pos(p, lane, q_len, L);
     float sl2 = p.scale_log2;
     if constexpr (FP8) sl2 *= *p.k_scale;
     const int32_t* bt_row = PAGED ? p.bt + (int64_t)r * p.bt_stride : nullptr;
@@ -385,8 +402,8 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage
             page_for(t_cur + 2 * step, pg);
             DT::load(p, lane, rows, kh, kr, vr);
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
-            DT::template compute<VAR>(stage, lane, t_cur, lo, limit, sl2, p.softcap_l2, p.softcap_inv2, qf, m_run,
-                                      l_run, oacc);
+            DT::template compute<VAR>(stage, lane, t_cur, lo, limit, sl2, p.softcap_l2, p.softcap_inv2, al2, qpos,
+                                      qf, m_run, l_run, oacc);
             row_from(t_cur + 2 * step, pg, rows);
             t_cur += step;
             if (t_cur >= k_end) break;
@@ -677,8 +694,8 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
     // within the register file)
     constexpr bool QN = RB == 1;
     u32x4 qf[RB][DT::KS], qn[DT::KS];
-    int limit[RB], lo[RB];
-    float sk[RB], sk_next[RB], m_run[RB], l_run[RB];
+    int limit[RB], lo[RB], qpos[RB];
+    float sk[RB], sk_next[RB], m_run[RB], l_run[RB], al2[RB];
     f32x4 oacc[RB][MB];
     const bool has_sinks = p.sinks != nullptr;
     auto head_of = [&](int kh, int rb) { return kh * p.g + (16 * rb + row) % p.g; };
@@ -687,6 +704,8 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
         load_decode_q<HD>(p, lane, c0.q0, c0.q_len * p.g, c0.kh, qf[rb], 16 * rb);
         limit[rb] = decode_row_limit(p, lane, c0.q_len, c0.L, 16 * rb);
         lo[rb] = VAR ? decode_row_lo(p, lane, c0.q_len, c0.L, 16 * rb) : 0;
+        al2[rb] = VAR ? decode_row_alibi(p, lane, c0.kh, 16 * rb) : 0.f;
+        qpos[rb] = decode_row_pos(p, lane, c0.q_len, c0.L, 16 * rb);
         sk[rb] = has_sinks ? sink_l2(p, head_of(c0.kh, rb)) : -INFINITY;
         sk_next[rb] = -INFINITY;
         m_run[rb] = -INFINITY;
@@ -788,7 +807,7 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
         for (int rb = 0; rb < RB; ++rb)
             if (rb == 0 || 16 * rb < c0.q_len * p.g)  // (a block without rows keeps its empty state)
                 DT::template compute<VAR>(stage, lane, c0.key0(), lo[rb], limit[rb], sl2, p.softcap_l2,
-                                          p.softcap_inv2, qf[rb], m_run[rb], l_run[rb], oacc[rb]);
+                                          p.softcap_inv2, al2[rb], qpos[rb], qf[rb], m_run[rb], l_run[rb], oacc[rb]);
         if (!c1.valid || c1_new) {
             close(c0);
             pending = true;
@@ -811,7 +830,11 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
                     sk[rb] = has_sinks ? sink_l2(p, head_of(c0.kh, rb)) : -INFINITY;
                 }
                 limit[rb] = decode_row_limit(p, lane, c0.q_len, c0.L, 16 * rb);
-                if constexpr (VAR) lo[rb] = decode_row_lo(p, lane, c0.q_len, c0.L, 16 * rb);
+                if constexpr (VAR) {
+                    lo[rb] = decode_row_lo(p, lane, c0.q_len, c0.L, 16 * rb);
+                    al2[rb] = decode_row_alibi(p, lane, c0.kh, 16 * rb);
+                }
+                qpos[rb] = decode_row_pos(p, lane, c0.q_len, c0.L, 16 * rb);
             }
             seg_t0 = 0;
         }
@@ -1021,9 +1044,12 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         vsc = *p.v_scale;
     }
     if constexpr (Q8) sl2 *= *p.q_scale;
-    // With the soft cap the scores are scaled and capped in place (log2
-    // domain) before the mask, and the softmax then takes them with scale 1.
-    const bool capped = VAR && p.softcap_l2 > 0.f;
+    // With the soft cap or ALiBi the scores are scaled, capped and biased in
+    // place (log2 domain) before the mask, and the softmax then takes them
+    // with scale 1.
+    const float al2 = VAR ? alibi_l2(p, head) : 0.f;  // this row's ALiBi slope
+    const int qpos = ctx + tl;                         // and its sequence position
+    const bool capped = VAR && (p.softcap_l2 > 0.f || p.alibi);
     const float sl2_cap = sl2;
     if (capped) sl2 = 1.f;
 
@@ -1177,13 +1203,20 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
                     qf[ks], sacc[kb]);
         }
     };
-    // soft cap of a tile's scores (before the mask)
-    auto cap = [&](f32x16 (&sacc)[KB]) {
+    // soft cap and ALiBi bias of the scores of the tile starting at key t0
+    // (before the mask), taking them to the log2 domain
+    auto cap = [&](int t0, f32x16 (&sacc)[KB]) {
         if (capped) {
+            const bool sc = p.softcap_l2 > 0.f;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) sacc[kb][e] = softcap_l2(sacc[kb][e] * sl2_cap, p.softcap_l2, p.softcap_inv2);
+                for (int e = 0; e < 16; ++e) {
+                    float x = sacc[kb][e] * sl2_cap;
+                    if (sc) x = softcap_l2(x, p.softcap_l2, p.softcap_inv2);
+                    const int key = t0 + kb * 32 + (e >> 2) * 8 + (e & 3) + hsel * 4;
+                    sacc[kb][e] = x - al2 * fabsf((float)(qpos - key));
+                }
         }
     };
     // causal / length mask of a tile that reaches past wave_min, window mask
@@ -1287,7 +1320,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         qk(k_lds0, s_a);
-        cap(s_a);
+        cap(k_begin, s_a);
         mask(k_begin, s_a);
         mx = rowmax(s_a);
         rescale(mx);
@@ -1318,7 +1351,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
             // (the mask branch comes after PV so that the S^T MFMAs of tile
             // i+1, the exponentials and the PV MFMAs of tile i share one
             // basic block for the scheduler)
-            cap(sn);
+            cap(t0 + TILE, sn);
             mask(t0 + TILE, sn);
             mx = rowmax(sn);
             rescale(mx);  // (here rather than before the exponentials: its branch stays out of that block)
@@ -1432,6 +1465,7 @@ __global__ __launch_bounds__(64) void generic_kernel(FwdParams p) {
         for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
         float x = dot * sl2;
         if (p.softcap_l2 > 0.f) x = softcap_l2(x, p.softcap_l2, p.softcap_inv2);
+        if (p.alibi) x -= alibi_l2(p, h) * fabsf((float)(L - q_len + t - j));
         const float m_new = fmaxf(m, x);
         const float alpha = fast_exp2(m - m_new);
         const float pj = fast_exp2(x - m_new);
@@ -1678,7 +1712,7 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, float* out_lse, c
 // ----------------------------------------------------------------- launchers
 
 // The decode kernels are built with and without the window / soft cap code.
-static bool uses_var(const FwdParams& p) { return p.window_left >= 0 || p.softcap_l2 > 0.f; }
+static bool uses_var(const FwdParams& p) { return p.window_left >= 0 || p.softcap_l2 > 0.f || p.alibi; }
 template <typename K1, typename K0>
 static void launch_var(K1 with_var, K0 plain, bool var, dim3 grid, hipStream_t s, const FwdParams& p) {
     if (var) hipLaunchKernelGGL(with_var, grid, dim3(256), 0, s, p);

@@ -38,6 +38,7 @@ struct FwdParams {
     float softcap_l2;         // softcap * log2(e) (> 0), or 0: no soft cap
     float softcap_inv2;       // 2 / softcap (soft cap on)
     const float* sinks;       // [H] natural-log sink logits, or nullptr
+    const float* alibi;       // [H] ALiBi slopes, or nullptr
 };
 
 enum class KvType { BF16, FP8, F32 };

@@ -70,8 +70,9 @@ class GpuProblem:
         pkv.pkv_cache_write(to_dev(p.kv_src_k[rows]), to_dev(p.kv_src_v[rows]), self.kc, self.vc,
                             to_dev(p.kv_slots[rows]), self.k_scale, self.v_scale)
 
-    def run(self, num_splits=0, causal=None, block_table=None, sliding_window=0, softcap=0.0, sinks=None):
-        """One forward; ``sinks`` is a host float32 array [H] (or None)."""
+    def run(self, num_splits=0, causal=None, block_table=None, sliding_window=0, softcap=0.0, sinks=None,
+            alibi=None):
+        """One forward; ``sinks`` and ``alibi`` (slopes) are host float32 arrays [H] (or None)."""
         p = self.prob
         bt = self.bt if block_table is None else block_table
         return pkv.pkv_varlen_fwd(self.q, self.kc, self.vc, self.qsl, self.seq_lens, bt, p.max_seqlen_q,
@@ -79,7 +80,8 @@ class GpuProblem:
                                   causal=p.causal if causal is None else causal, k_scale=self.k_scale,
                                   v_scale=self.v_scale, num_splits=num_splits, return_lse=True,
                                   sliding_window=sliding_window, softcap=softcap, q_scale=self.q_scale,
-                                  sinks=None if sinks is None else to_dev(np.asarray(sinks, np.float32)))
+                                  sinks=None if sinks is None else to_dev(np.asarray(sinks, np.float32)),
+                                  alibi_slopes=None if alibi is None else to_dev(np.asarray(alibi, np.float32)))
 
 
 def oracle_cache(prob, requests=None):
@@ -99,11 +101,13 @@ def requests_of(prob, rows):
     return np.unique(np.searchsorted(prob.query_start_loc, np.asarray(rows), side="right") - 1)
 
 
-def oracle_attention(prob, rows=None, causal=None, caches=None, sliding_window=0, softcap=0.0, sinks=None):
+def oracle_attention(prob, rows=None, causal=None, caches=None, sliding_window=0, softcap=0.0, sinks=None,
+                     alibi=None):
     """The oracle's answer; a sliding window of w keys is its window_left = w - 1."""
     causal = prob.causal if causal is None else causal
     var = dict(window_left=sliding_window - 1 if sliding_window > 0 else -1, softcap=softcap,
-               sinks=None if sinks is None else np.asarray(sinks, np.float32).astype(np.float64))
+               sinks=None if sinks is None else np.asarray(sinks, np.float32).astype(np.float64),
+               alibi=None if alibi is None else np.asarray(alibi, np.float32).astype(np.float64))
     if not prob.paged:
         flat = np.concatenate(prob.pos_rows)
         return oracle.attention(prob.q, prob.kv_src_k[flat], prob.kv_src_v[flat], prob.query_start_loc,

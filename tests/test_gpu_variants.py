@@ -1,5 +1,5 @@
 """GPU parity of the attention variants (sliding window, logits soft cap,
-attention sinks), alone and together, against the float64 oracle, for every
+attention sinks, ALiBi), alone and together, against the float64 oracle, for every
 kernel family: balanced and split decode, split and unsplit prefill (causal
 and not), the generic kernel, an fp8 cache and the cascade.
 
@@ -32,6 +32,12 @@ def sinks_for(H, seed):
     return s
 
 
+def alibi_for(H):
+    """The usual geometric ALiBi slopes 2^(-8 (h + 1) / H): the first head's
+    bias falls by most of a unit per key, the last one's by 2^-8."""
+    return (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
+
+
 VARIANTS = {
     "window64": dict(sliding_window=64),
     "window1": dict(sliding_window=1),           # a query sees only its own key
@@ -41,6 +47,8 @@ VARIANTS = {
     "softcap_wide": dict(softcap=30.0),
     "sinks": dict(sinks=True),
     "all": dict(sliding_window=50, softcap=2.0, sinks=True),
+    "alibi": dict(alibi=True),
+    "alibi_all": dict(sliding_window=70, softcap=2.0, sinks=True, alibi=True),
 }
 
 
@@ -48,6 +56,8 @@ def run_variant(prob, var, num_splits=0, causal=None, seed=0, out_tol=None, what
     var = dict(var)
     if var.pop("sinks", False):
         var["sinks"] = sinks_for(prob.H, seed)
+    if var.pop("alibi", False):
+        var["alibi"] = alibi_for(prob.H)
     g = GpuProblem(prob)
     out, lse = g.run(num_splits=num_splits, causal=causal, **var)
     torch.cuda.synchronize()
@@ -88,7 +98,8 @@ PREFILL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("vname", ["window64", "window1", "window37", "softcap", "sinks", "all"])
+@pytest.mark.parametrize("vname", ["window64", "window1", "window37", "softcap", "sinks", "all", "alibi",
+                                   "alibi_all"])
 @pytest.mark.parametrize("case", PREFILL_CASES)
 @pytest.mark.parametrize("num_splits", [1, 4])
 @pytest.mark.parametrize("causal", [True, False])
@@ -105,7 +116,7 @@ GENERIC_CASES = [
 ]
 
 
-@pytest.mark.parametrize("vname", ["window1", "window37", "softcap", "sinks", "all"])
+@pytest.mark.parametrize("vname", ["window1", "window37", "softcap", "sinks", "all", "alibi", "alibi_all"])
 @pytest.mark.parametrize("case", GENERIC_CASES)
 @pytest.mark.parametrize("num_splits", [1, 2])
 def test_generic_variant(case, vname, num_splits):
@@ -115,7 +126,7 @@ def test_generic_variant(case, vname, num_splits):
     run_variant(prob, VARIANTS[vname], num_splits, seed=hd, what=f"generic {case} {vname}")
 
 
-@pytest.mark.parametrize("vname", ["window64", "softcap", "sinks", "all"])
+@pytest.mark.parametrize("vname", ["window64", "softcap", "sinks", "all", "alibi"])
 @pytest.mark.parametrize("bs", [1, 16, 256])
 def test_fp8_decode_variant(vname, bs):
     prob = workloads.make_problem(950, [1] * 6, [40, 300, 1023, 7, 260, 513], H=32, Hkv=8, hd=128, bs=bs,
@@ -123,7 +134,7 @@ def test_fp8_decode_variant(vname, bs):
     run_variant(prob, VARIANTS[vname], 0, seed=bs, what=f"fp8 decode bs={bs} {vname}")
 
 
-@pytest.mark.parametrize("vname", ["window64", "all"])
+@pytest.mark.parametrize("vname", ["window64", "all", "alibi_all"])
 def test_fp8_prefill_variant(vname):
     prob = workloads.make_problem(951, [70, 33], [100, 0], H=8, Hkv=2, hd=128, bs=16, cache_dtype="fp8")
     run_variant(prob, VARIANTS[vname], 1, seed=3, what=f"fp8 prefill {vname}")
@@ -202,3 +213,24 @@ def test_dominant_sink():
         torch.cuda.synchronize()
         assert np.abs(out_f64(out)).max() < 1e-18
         np.testing.assert_allclose(lse.cpu().numpy(), 60.0, atol=1e-3)
+
+
+def test_alibi_small_slopes_reach_far():
+    """Slopes of 1e-3 per key move the softmax over contexts of thousands of
+    keys without collapsing it onto the diagonal: every kernel family agrees
+    with the oracle on long decode and chunked-prefill requests."""
+    prob = workloads.make_problem(965, [1, 1, 64, 1], [4000, 2500, 3000, 64], H=16, Hkv=4, hd=128, bs=16)
+    slopes = np.linspace(1e-4, 2e-3, 16).astype(np.float32)
+    ref, ref_lse = oracle_attention(prob, alibi=slopes)
+    g = GpuProblem(prob)
+    for ns in (0, 1, 4):
+        out, lse = g.run(num_splits=ns, alibi=slopes)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, ref, ref_lse, BF16_OUT, BF16_LSE, what=f"alibi small slopes splits={ns}")
+
+
+def test_alibi_rejects_wrong_length():
+    prob = workloads.make_problem(966, [1], [10], H=8, Hkv=2, hd=128, bs=16)
+    g = GpuProblem(prob)
+    with pytest.raises(ValueError):
+        g.run(alibi=np.ones(4, np.float32))
