@@ -301,7 +301,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the attention shards by request "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the attention shards by request "
               "or kv head with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

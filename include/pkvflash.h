@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
     PKV_OK = 0,
     PKV_ERR_INVALID_ARG = 1,  /* a null pointer, a negative or inconsistent size */
-    PKV_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (dtype pair, head size) */
+    PKV_ERR_UNSUPPORTED = 2,  /* a valid request the library does not implement (dtype pair, head size) */
     PKV_ERR_WORKSPACE = 3,    /* the split-KV workspace is missing or too small */
     PKV_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
 } pkv_status;

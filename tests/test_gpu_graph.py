@@ -73,7 +73,14 @@ def test_graph_balanced_decode():
 def test_graph_multi_row_decode_with_variants():
     prob = workloads.make_problem(1300, [5, 8, 1, 3], [200, 900, 40, 1000], H=32, Hkv=8, hd=128, bs=16)
     sinks = to_dev(np.random.default_rng(1).normal(0, 2, 32).astype(np.float32))
-    replay_matches_eager(*make_step(prob, sliding_window=100, softcap=5.0, sinks=sinks))
+    slopes = to_dev((2.0 ** (-8.0 * (np.arange(32) + 1) / 32)).astype(np.float32))
+    replay_matches_eager(*make_step(prob, sliding_window=100, softcap=5.0, sinks=sinks, alibi_slopes=slopes))
+
+
+def test_graph_prefill_with_variants():
+    prob = workloads.chunked_prefill(seed=1304, B=3, qlo=40, qhi=300, clo=0, chi=500)
+    slopes = to_dev((2.0 ** (-8.0 * (np.arange(prob.H) + 1) / prob.H)).astype(np.float32))
+    replay_matches_eager(*make_step(prob, num_splits=1, sliding_window=200, alibi_slopes=slopes))
 
 
 @pytest.mark.parametrize("num_splits", [1, 3])
