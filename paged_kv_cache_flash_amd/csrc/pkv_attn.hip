@@ -552,7 +552,6 @@ struct DecodeCursor {
 template <int HD, bool FP8, bool PAGED, bool VAR, int RB>
 __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_balanced_kernel(FwdParams p) {
     using DT = DecodeTile<HD, FP8>;
-    constexpr int TILE = kDecodeTile;
     constexpr int MB = DT::MB;
     constexpr int NL = DT::NL;
     constexpr int ROWS = 16 * RB;
@@ -956,7 +955,6 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     constexpr int MB = HD / 32;                 // 32-row blocks of O^T
     constexpr int KB = TILE / 32;               // 32-key blocks per tile
     constexpr int SLOT = TILE / PT::KPI * PT::GP;  // bytes of one K or V tile
-    constexpr int ESZ = FP8 ? 1 : 2;            // bytes per cached element
     static_assert(TILE == kTileRows && CPW >= 1 && FCPW >= 1 && KPI == PT::KPI, "");
     static_assert(!Q8 || (FP8 && HD == 128 && FPR == 8), "the fp8 MFMA mode is built for head size 128");
     // K tile j in k_lds<j % 2>, V tile j in v_lds<j % 2>; four separate arrays
@@ -1792,8 +1790,7 @@ hipError_t launch_decode(const FwdParams& p, KvType kv, hipStream_t s) {
 template <int HD>
 static hipError_t prefill_hd(const FwdParams& p, KvType kv, bool q8, hipStream_t s) {
     const int64_t streams_per_xcd = ((int64_t)p.B * p.Hkv + kXcds - 1) / kXcds;
-    dim3 grid((unsigned)(streams_per_xcd * kXcds * p.n_qtiles), p.num_splits);
-    const dim3 block(64 * kPrefillWaves);
+    dim3 grid((unsigned)(streams_per_xcd * kXcds * p.n_qtiles), p.num_splits);  // 64 * kPrefillWaves threads each
     const int pg = !p.bt ? kPgFlat : (p.bs_shift >= 4 ? kPgWide : kPgAny);
     const bool var = uses_var(p);
     if constexpr (HD == 128) {
