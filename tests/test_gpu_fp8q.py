@@ -45,14 +45,16 @@ def test_fp8_q_parity(case, num_splits, causal):
     assert_parity(out, lse, ref, ref_lse, FP8_OUT, LSE, what=f"fp8 q {case} splits={num_splits} causal={causal}")
 
 
-@pytest.mark.parametrize("var", [dict(sliding_window=40), dict(softcap=2.0), dict(sinks=True),
-                                 dict(sliding_window=64, softcap=1.5, sinks=True)])
+@pytest.mark.parametrize("var", [dict(sliding_window=40), dict(softcap=2.0), dict(sinks=True), dict(alibi=True),
+                                 dict(sliding_window=64, softcap=1.5, sinks=True, alibi=True)])
 def test_fp8_q_variants(var):
     prob = workloads.make_problem(1150, [200, 64, 9], [300, 17, 1000], H=32, Hkv=8, hd=128, bs=16, q_dtype="fp8",
                                   cache_dtype="fp8")
     var = dict(var)
     if var.pop("sinks", False):
         var["sinks"] = np.random.default_rng(3).normal(1.5, 2.0, prob.H).astype(np.float32)
+    if var.pop("alibi", False):
+        var["alibi"] = (2.0 ** (-8.0 * (np.arange(prob.H) + 1) / prob.H)).astype(np.float32)
     g = GpuProblem(prob)
     for ns in (1, 3):
         out, lse = g.run(num_splits=ns, **var)

@@ -15,6 +15,8 @@ Workloads (seeded, synthetic; the recipes are in workloads/):
   * encoder: 16 requests of U[512, 4096] tokens, non-causal, flat K/V, 32 heads MHA
   * fp8 e4m3fn decode: batch 128, context U[1024, 8192], 32/8 heads, swept
     over page sizes 1, 8, 16, 64 and 256 (the same logical K/V each time)
+  * multi-token decode: batch 64, q_len U[2, 16] on context U[512, 4096], 32/8 heads, page 16
+  * chunked prefill over an fp8 e4m3fn cache, with a bf16 q and with an e4m3fn q
 """
 import numpy as np
 import pytest
@@ -117,3 +119,18 @@ def test_full_fp8_decode_page_sweep(fp8_batch, bs):
     check_whole_output(prob, out, lse)
     ref, ref_lse = oracle_attention(prob, rows=rows, caches=oracle_cache(prob, requests_of(prob, rows)))
     assert_parity(out, lse, ref, ref_lse, FP8_OUT, BF16_LSE, rows=rows, what=f"fp8 decode bs={bs}")
+
+
+def test_full_spec_decode():
+    prob = workloads.spec_decode(bs=16)
+    run_full(prob, sample_rows(prob, 32, 6), BF16_OUT, "multi-token decode")
+
+
+def test_full_fp8kv_prefill():
+    prob = workloads.chunked_prefill(bs=16, cache_dtype="fp8")
+    run_full(prob, sample_rows(prob, 24, 7), FP8_OUT, "chunked prefill, fp8 cache")
+
+
+def test_full_fp8q_prefill():
+    prob = workloads.chunked_prefill(bs=16, cache_dtype="fp8", q_dtype="fp8")
+    run_full(prob, sample_rows(prob, 24, 8), FP8_OUT, "chunked prefill, fp8 q and cache")
