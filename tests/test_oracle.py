@@ -350,6 +350,43 @@ def test_oracle_matches_torch_sdpa_float64(case):
             np.testing.assert_allclose(out[q0:q1], ref2.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("window", [0, 3])
+def test_oracle_alibi_and_window_match_torch_sdpa_float64(case, window):
+    """ALiBi and the sliding window through torch's SDPA with an additive
+    float mask: the bias -slope_h |i - j| on every visible (query position i,
+    key j) pair, -inf where the causal bound or the window hides the key."""
+    prob = workloads.make_problem(case["seed"], case["q"], case["c"], H=case["H"], Hkv=case["Hkv"],
+                                  hd=case["hd"], bs=case["bs"])
+    slopes = 0.5 ** (1.0 + np.arange(prob.H))
+    kc, vc = prob.empty_cache()
+    kc, vc = oracle.cache_write(prob.kv_src_k, prob.kv_src_v, kc, vc, prob.kv_slots, prob.bs)
+    out, _ = oracle.attention(prob.q, kc, vc, prob.query_start_loc, prob.seq_lens, prob.block_table,
+                              scale=prob.scale, causal=True, window_left=window - 1 if window else -1, alibi=slopes)
+    kf, vf, loc = prob.flat_kv()
+    qd = torch.from_numpy(workloads.bf16_bits_to_f32(prob.q).astype(np.float64))
+    kd = torch.from_numpy(workloads.bf16_bits_to_f32(kf).astype(np.float64))
+    vd = torch.from_numpy(workloads.bf16_bits_to_f32(vf).astype(np.float64))
+    g = prob.H // prob.Hkv
+    for r in range(prob.B):
+        q0, q1 = prob.query_start_loc[r], prob.query_start_loc[r + 1]
+        if q1 == q0:
+            continue
+        qn, L = q1 - q0, loc[r + 1] - loc[r]
+        Q = qd[q0:q1].transpose(0, 1)
+        K = kd[loc[r]:loc[r + 1]].transpose(0, 1).repeat_interleave(g, 0).contiguous()
+        V = vd[loc[r]:loc[r + 1]].transpose(0, 1).repeat_interleave(g, 0).contiguous()
+        i = (L - qn + torch.arange(qn, dtype=torch.float64))[:, None]
+        j = torch.arange(L, dtype=torch.float64)[None, :]
+        visible = j <= i
+        if window:
+            visible &= j >= i - (window - 1)
+        bias = -torch.from_numpy(slopes)[:, None, None] * (i - j).abs()[None]
+        mask = torch.where(visible[None], bias, torch.tensor(-np.inf, dtype=torch.float64))
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=prob.scale)
+        np.testing.assert_allclose(out[q0:q1], ref.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+
+
 # --------------------------------------------------------------- invariants
 
 def test_paged_equals_contiguous():
