@@ -151,6 +151,15 @@ __device__ __forceinline__ void finalize_row(float m, float l, float sink2, floa
 
 // ----------------------------------------------------------------- decode
 
+// One 16-byte global -> LDS copy per lane, written by the load unit straight
+// into LDS at lds_base + 16 * lane (lds_base must be wave-uniform); `off` is
+// added to the global address.
+template <int OFF>
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, OFF, 0);
+}
+
 // One decode wave's 32-key tile: loads, LDS staging and compute. The LDS area
 // of a wave holds the tile's K and V row-major in bf16. The K pitch (HD + 8
 // elements) puts consecutive rows 16 bytes apart in bank space, so the
@@ -175,6 +184,32 @@ struct DecodeTile {
 
     // Key (within the tile) that load i of `lane` reads.
     static __device__ __forceinline__ int key_of(int lane, int i) { return lane / GPR + KPL * i; }
+
+    // bf16 tiles of head size 128 can go straight from the cache into LDS
+    // (global_load_lds, no registers on the way), into two stages per wave so
+    // that the next tile lands while this one is computed. A K or V tile is
+    // then 32 rows of 256 bytes, row r at 256 r with its 16-byte chunk c at
+    // position c ^ dsw(r) (each copy lane fetches the chunk its position
+    // needs). dsw permutes the low four row bits so that the 16 rows of a K
+    // operand read (one chunk each) and the 8 rows of 32 lanes' transposed V
+    // reads (two chunks each) hit every one of the 64 banks once.
+    static constexpr bool DMA = !FP8 && HD == 128;
+    static constexpr int DMA_TILE = TILE * HD * 2;      // bytes of a K or V tile
+    static constexpr int DMA_STAGE = 2 * DMA_TILE;      // K then V
+    static __device__ __forceinline__ int dsw(int r) {
+        return (((r >> 2) & 1) << 3) | (((r >> 1) & 1) << 2) | ((r & 1) << 1) | ((r >> 3) & 1);
+    }
+    static __device__ __forceinline__ void issue(const FwdParams& p, int lane, const int (&rows)[NL], int kh,
+                                                 uint8_t* st) {
+        const int64_t rstride = (int64_t)p.Hkv * HD;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int chunk = (lane % GPR) ^ dsw(key_of(lane, i) & 15);
+            const int64_t e = (int64_t)rows[i] * rstride + (int64_t)kh * HD + chunk * EPL;
+            copy16_to_lds<0>((const uint16_t*)p.k_cache + e, st + i * 1024);
+            copy16_to_lds<0>((const uint16_t*)p.v_cache + e, st + DMA_TILE + i * 1024);
+        }
+    }
 
     // K and V of a tile with row-coalesced 16-byte loads: load i of lane l
     // covers granule c = l + 64 i, i.e. key c / GPR, elements (c % GPR) * EPL
@@ -223,23 +258,30 @@ struct DecodeTile {
     // qpos),
     // online softmax, then O^T += V^T P^T with V^T read transposed. m_run is
     // row-uniform (log2 domain), l_run per lane (this lane's keys only).
-    template <bool VAR>
+    // (DL: the tile is in the global_load_lds layout above)
+    template <bool VAR, bool DL = false>
     static __device__ __forceinline__ void compute(const uint16_t* stage, int lane, int t0, int lo, int limit,
                                                    float sl2, float cap_l2, float cap_inv2, float al2, int qpos,
                                                    const u32x4 (&qf)[KS], float& m_run, float& l_run,
                                                    f32x4 (&oacc)[MB]) {
         const uint16_t* const kl = stage;
         const uint16_t* const vl = stage + K_ELEMS;
+        const uint8_t* const st = (const uint8_t*)stage;
         const int row = lane & 15;
         const int G = lane >> 4;
         f32x4 sacc[2];
         const uint16_t* kp = kl + row * KP + G * 8;
+        // DL: row b 16 + row, chunk G + 4 ks at position (G + 4 ks) ^ dsw(row)
+        const int swk = dsw(row);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             sacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                sacc[b] = mfma16x16x32(*(const u32x4*)(kp + b * 16 * KP + ks * 32), qf[ks], sacc[b]);
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 kf = DL ? *(const u32x4*)(st + (b * 16 + row) * 256 + (((G + 4 * ks) ^ swk) << 4))
+                                    : *(const u32x4*)(kp + b * 16 * KP + ks * 32);
+                sacc[b] = mfma16x16x32(kf, qf[ks], sacc[b]);
+            }
         }
         float sv[8];
         float mx = -INFINITY;
@@ -278,10 +320,22 @@ struct DecodeTile {
         const u32x4 pf = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]), pack_bf16x2(sv[4], sv[5]),
                           pack_bf16x2(sv[6], sv[7])};
         const uint16_t* vt = vl + (G * 4 + ((lane & 15) >> 2)) * VP + (lane & 3) * 4;
+        // DL: row R (and R + 16), bytes 32 mb + 8 (lane & 3) onward: chunk
+        // 2 mb + (lane & 3) / 2 at position chunk ^ dsw(R), half lane & 1
+        const int rv = G * 4 + ((lane & 15) >> 2);
+        const int swv = dsw(rv);
+        const uint8_t* const vst = st + DMA_TILE + rv * 256 + (lane & 1) * 8;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const u32x2 lo = lds_read_tr16(vt + mb * 16);
-            const u32x2 hi = lds_read_tr16(vt + 16 * VP + mb * 16);
+            u32x2 lo, hi;
+            if constexpr (DL) {
+                const int pos = ((2 * mb + ((lane & 3) >> 1)) ^ swv) << 4;
+                lo = lds_read_tr16(vst + pos);
+                hi = lds_read_tr16(vst + 16 * 256 + pos);
+            } else {
+                lo = lds_read_tr16(vt + mb * 16);
+                hi = lds_read_tr16(vt + 16 * VP + mb * 16);
+            }
             oacc[mb] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, oacc[mb]);
         }
     }
@@ -555,7 +609,11 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
     constexpr int MB = DT::MB;
     constexpr int NL = DT::NL;
     constexpr int ROWS = 16 * RB;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * DT::ELEMS];
+    // tiles straight into LDS, two stages per wave (one row block only: with
+    // more, the register file is the constraint and the staged copy is faster)
+    constexpr bool DMA = DT::DMA && RB == 1;
+    constexpr int SMEM = DMA ? 4 * 2 * DT::DMA_STAGE : 4 * DT::ELEMS * 2;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
     const int64_t gw = (int64_t)blockIdx.x * 4 + w;
@@ -678,7 +736,8 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
         }
     };
 
-    uint16_t* const stage = smem + w * DT::ELEMS;
+    uint16_t* const stage = (uint16_t*)smem + w * DT::ELEMS;
+    uint8_t* const dstage = smem + w * 2 * DT::DMA_STAGE;  // (DMA) stage 0, then stage 1
     float sl2 = p.scale_log2;
     if constexpr (FP8) sl2 *= *p.k_scale;
     const float vsc = FP8 ? *p.v_scale : 1.f;
@@ -780,20 +839,28 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
     // if it ends there, and moves tile i+1 into LDS. A new item therefore
     // costs no pipeline restart. Past the wave's range the last tile is
     // re-read (cached) and never computed.
-    u32x4 kr[NL], vr[NL];
+    u32x4 kr[DMA ? 1 : NL], vr[DMA ? 1 : NL];
     int pg[NL], rows[NL];
+    int par = 0;  // (DMA) stage of the tile being computed
     page_for(c0, pg);
     row_from(c0, pg, rows);
     page_for(c1, pg);
-    DT::load(p, lane, rows, c0.kh, kr, vr);
+    if constexpr (DMA) DT::issue(p, lane, rows, c0.kh, dstage);
+    else DT::load(p, lane, rows, c0.kh, kr, vr);
     row_from(c1, pg, rows);
-    DT::store(stage, lane, kr, vr);
+    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    else DT::store(stage, lane, kr, vr);
     bool pending = false;
     while (true) {
         if (pending) write();
         pending = false;
         page_for(c2, pg);
-        DT::load(p, lane, rows, c1.kh, kr, vr);
+        if constexpr (DMA) {
+            wave_lds_sync();  // (the other stage's last reads are done)
+            DT::issue(p, lane, rows, c1.kh, dstage + (par ^ 1) * DT::DMA_STAGE);
+        } else {
+            DT::load(p, lane, rows, c1.kh, kr, vr);
+        }
         const bool c1_new = c1.valid && c1.t == 0;
         if constexpr (QN) {
             if (c1_new) {
@@ -805,8 +872,9 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
             if (rb == 0 || 16 * rb < c0.q_len * p.g)  // (a block without rows keeps its empty state)
-                DT::template compute<VAR>(stage, lane, c0.key0(), lo[rb], limit[rb], sl2, p.softcap_l2,
-                                          p.softcap_inv2, al2[rb], qpos[rb], qf[rb], m_run[rb], l_run[rb], oacc[rb]);
+                DT::template compute<VAR, DMA>(DMA ? (const uint16_t*)(dstage + par * DT::DMA_STAGE) : stage, lane,
+                                               c0.key0(), lo[rb], limit[rb], sl2, p.softcap_l2, p.softcap_inv2,
+                                               al2[rb], qpos[rb], qf[rb], m_run[rb], l_run[rb], oacc[rb]);
         if (!c1.valid || c1_new) {
             close(c0);
             pending = true;
@@ -837,12 +905,14 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
             }
             seg_t0 = 0;
         }
-        DT::store(stage, lane, kr, vr);
+        if constexpr (!DMA) DT::store(stage, lane, kr, vr);
         // Nothing may be left in flight here: the next iteration's loads are
         // then the only ones its waits count (the query loads would otherwise
-        // make the compiler wait on every tile load it issues).
+        // make the compiler wait on every tile load it issues). With DMA this
+        // is also where the next tile has landed in the other stage.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __builtin_amdgcn_sched_barrier(0);
+        par ^= 1;
     }
     write();  // the wave's last segment
 }
@@ -855,14 +925,6 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
 // stale maximum keeps the result exact.
 constexpr float kLazyRescale = 8.f;
 
-// One 16-byte global -> LDS copy per lane, written by the load unit straight
-// into LDS at lds_base + 16 * lane (lds_base must be wave-uniform); `off` is
-// added to the global address.
-template <int OFF>
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, OFF, 0);
-}
 
 // K/V tiles of 64 keys live in LDS row-major (a key's head_size bf16
 // elements contiguous). A 64-lane tile copy moves whole cache rows: each group
