@@ -185,29 +185,33 @@ struct DecodeTile {
     // Key (within the tile) that load i of `lane` reads.
     static __device__ __forceinline__ int key_of(int lane, int i) { return lane / GPR + KPL * i; }
 
-    // bf16 tiles of head size 128 can go straight from the cache into LDS
+    // Tiles of head size 128 can go straight from the cache into LDS
     // (global_load_lds, no registers on the way), into two stages per wave so
     // that the next tile lands while this one is computed. A K or V tile is
-    // then 32 rows of 256 bytes, row r at 256 r with its 16-byte chunk c at
-    // position c ^ dsw(r) (each copy lane fetches the chunk its position
-    // needs). dsw permutes the low four row bits so that the 16 rows of a K
-    // operand read (one chunk each) and the 8 rows of 32 lanes' transposed V
-    // reads (two chunks each) hit every one of the 64 banks once.
-    static constexpr bool DMA = !FP8 && HD == 128;
-    static constexpr int DMA_TILE = TILE * HD * 2;      // bytes of a K or V tile
+    // then 32 rows of 256 bytes (bf16) or 128 bytes (fp8, kept as bytes and
+    // widened as it is read), row r at its row offset with its 16-byte chunk
+    // c at position c ^ dsw(r) (each copy lane fetches the chunk its position
+    // needs). dsw permutes row bits so that the rows of a K operand read and
+    // of 32 lanes' transposed V reads hit every one of the 64 banks once.
+    static constexpr bool DMA = HD == 128;
+    static constexpr int RB_ = HD * ESZ;                // bytes of a row
+    static constexpr int DMA_TILE = TILE * RB_;         // bytes of a K or V tile
     static constexpr int DMA_STAGE = 2 * DMA_TILE;      // K then V
     static __device__ __forceinline__ int dsw(int r) {
-        return (((r >> 2) & 1) << 3) | (((r >> 1) & 1) << 2) | ((r & 1) << 1) | ((r >> 3) & 1);
+        if constexpr (FP8)  // 8 chunks a row: the even (odd) rows of a read take 8 distinct positions
+            return ((r >> 1) & 3) | ((((r >> 3) ^ (r >> 4)) & 1) << 2);
+        else
+            return (((r >> 2) & 1) << 3) | (((r >> 1) & 1) << 2) | ((r & 1) << 1) | ((r >> 3) & 1);
     }
     static __device__ __forceinline__ void issue(const FwdParams& p, int lane, const int (&rows)[NL], int kh,
                                                  uint8_t* st) {
         const int64_t rstride = (int64_t)p.Hkv * HD;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int chunk = (lane % GPR) ^ dsw(key_of(lane, i) & 15);
-            const int64_t e = (int64_t)rows[i] * rstride + (int64_t)kh * HD + chunk * EPL;
-            copy16_to_lds<0>((const uint16_t*)p.k_cache + e, st + i * 1024);
-            copy16_to_lds<0>((const uint16_t*)p.v_cache + e, st + DMA_TILE + i * 1024);
+            const int chunk = (lane % GPR) ^ dsw(key_of(lane, i));
+            const int64_t e = ((int64_t)rows[i] * rstride + (int64_t)kh * HD + chunk * EPL) * ESZ;
+            copy16_to_lds<0>((const uint8_t*)p.k_cache + e, st + i * 1024);
+            copy16_to_lds<0>((const uint8_t*)p.v_cache + e, st + DMA_TILE + i * 1024);
         }
     }
 
@@ -271,15 +275,22 @@ struct DecodeTile {
         const int G = lane >> 4;
         f32x4 sacc[2];
         const uint16_t* kp = kl + row * KP + G * 8;
-        // DL: row b 16 + row, chunk G + 4 ks at position (G + 4 ks) ^ dsw(row)
-        const int swk = dsw(row);
+        // DL, bf16: row b 16 + row, chunk G + 4 ks at position (G + 4 ks) ^ dsw(row);
+        // fp8: bytes 32 ks + 8 G of the row, chunk 2 ks + G / 2, half G % 2
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             sacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int swk = dsw(b * 16 + row);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 kf = DL ? *(const u32x4*)(st + (b * 16 + row) * 256 + (((G + 4 * ks) ^ swk) << 4))
-                                    : *(const u32x4*)(kp + b * 16 * KP + ks * 32);
+                u32x4 kf;
+                if constexpr (DL && FP8)
+                    kf = fp8x8_to_bf16x8(*(const u32x2*)(st + (b * 16 + row) * RB_ +
+                                                         (((2 * ks + (G >> 1)) ^ swk) << 4) + (G & 1) * 8));
+                else if constexpr (DL)
+                    kf = *(const u32x4*)(st + (b * 16 + row) * RB_ + (((G + 4 * ks) ^ swk) << 4));
+                else
+                    kf = *(const u32x4*)(kp + b * 16 * KP + ks * 32);
                 sacc[b] = mfma16x16x32(kf, qf[ks], sacc[b]);
             }
         }
@@ -320,15 +331,22 @@ struct DecodeTile {
         const u32x4 pf = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]), pack_bf16x2(sv[4], sv[5]),
                           pack_bf16x2(sv[6], sv[7])};
         const uint16_t* vt = vl + (G * 4 + ((lane & 15) >> 2)) * VP + (lane & 3) * 4;
-        // DL: row R (and R + 16), bytes 32 mb + 8 (lane & 3) onward: chunk
-        // 2 mb + (lane & 3) / 2 at position chunk ^ dsw(R), half lane & 1
-        const int rv = G * 4 + ((lane & 15) >> 2);
+        // DL, bf16: row R (and R + 16), bytes 32 mb + 8 (lane & 3) onward:
+        // chunk 2 mb + (lane & 3) / 2 at position chunk ^ dsw(R), half lane & 1.
+        // fp8: one transposed byte read gives the 8 keys of the lane's k-slots;
+        // lane s of a 16-lane group addresses bytes 16 mb + 8 (s % 2) of the
+        // row of slot s / 2 (key 16 (j / 4) + 4 G + j % 4, j = s / 2).
+        const int rv = FP8 ? 16 * (((lane & 15) >> 1) >> 2) + 4 * G + (((lane & 15) >> 1) & 3)
+                           : G * 4 + ((lane & 15) >> 2);
         const int swv = dsw(rv);
-        const uint8_t* const vst = st + DMA_TILE + rv * 256 + (lane & 1) * 8;
+        const uint8_t* const vst = st + DMA_TILE + rv * RB_ + (lane & 1) * 8;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             u32x2 lo, hi;
-            if constexpr (DL) {
+            if constexpr (DL && FP8) {
+                oacc[mb] = mfma16x16x32(fp8x8_to_bf16x8(lds_read_tr8(vst + ((mb ^ swv) << 4))), pf, oacc[mb]);
+                continue;
+            } else if constexpr (DL) {
                 const int pos = ((2 * mb + ((lane & 3) >> 1)) ^ swv) << 4;
                 lo = lds_read_tr16(vst + pos);
                 hi = lds_read_tr16(vst + 16 * 256 + pos);
@@ -612,6 +630,7 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 ? 2 : 1) void decode_bala
     // tiles straight into LDS, two stages per wave (one row block only: with
     // more, the register file is the constraint and the staged copy is faster)
     constexpr bool DMA = DT::DMA && RB == 1;
+    static_assert(!DMA || DT::NL * 1024 == DT::DMA_TILE, "one 1 KB copy per load");
     constexpr int SMEM = DMA ? 4 * 2 * DT::DMA_STAGE : 4 * DT::ELEMS * 2;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
     const int lane = threadIdx.x & 63;

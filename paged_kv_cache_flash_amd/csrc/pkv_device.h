@@ -26,6 +26,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -53,6 +54,15 @@ __device__ __forceinline__ f32x16 mfma32x32x64_fp8(u32x4 a0, u32x4 a1, u32x4 b0,
 __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// Transposed 8-bit LDS read: in each group of 16 lanes, byte j of lane l's
+// result is byte l % 8 of the 8 bytes that lane 2 j + (l % 16) / 8 of the
+// group addresses.
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
     return __builtin_bit_cast(u32x2, r);
 }
 
