@@ -194,8 +194,8 @@ struct DecodeTile {
     // needs). dsw permutes row bits so that the rows of a K operand read and
     // of 32 lanes' transposed V reads hit every one of the 64 banks once.
     static constexpr bool DMA = HD == 128;
-    static constexpr int RB_ = HD * ESZ;                // bytes of a row
-    static constexpr int DMA_TILE = TILE * RB_;         // bytes of a K or V tile
+    static constexpr int ROW_BYTES = HD * ESZ;                // bytes of a row
+    static constexpr int DMA_TILE = TILE * ROW_BYTES;         // bytes of a K or V tile
     static constexpr int DMA_STAGE = 2 * DMA_TILE;      // K then V
     static __device__ __forceinline__ int dsw(int r) {
         if constexpr (FP8)  // 8 chunks a row: the even (odd) rows of a read take 8 distinct positions
@@ -285,10 +285,10 @@ struct DecodeTile {
             for (int ks = 0; ks < KS; ++ks) {
                 u32x4 kf;
                 if constexpr (DL && FP8)
-                    kf = fp8x8_to_bf16x8(*(const u32x2*)(st + (b * 16 + row) * RB_ +
+                    kf = fp8x8_to_bf16x8(*(const u32x2*)(st + (b * 16 + row) * ROW_BYTES +
                                                          (((2 * ks + (G >> 1)) ^ swk) << 4) + (G & 1) * 8));
                 else if constexpr (DL)
-                    kf = *(const u32x4*)(st + (b * 16 + row) * RB_ + (((G + 4 * ks) ^ swk) << 4));
+                    kf = *(const u32x4*)(st + (b * 16 + row) * ROW_BYTES + (((G + 4 * ks) ^ swk) << 4));
                 else
                     kf = *(const u32x4*)(kp + b * 16 * KP + ks * 32);
                 sacc[b] = mfma16x16x32(kf, qf[ks], sacc[b]);
@@ -339,22 +339,25 @@ struct DecodeTile {
         const int rv = FP8 ? 16 * (((lane & 15) >> 1) >> 2) + 4 * G + (((lane & 15) >> 1) & 3)
                            : G * 4 + ((lane & 15) >> 2);
         const int swv = dsw(rv);
-        const uint8_t* const vst = st + DMA_TILE + rv * RB_ + (lane & 1) * 8;
+        const uint8_t* const vst = st + DMA_TILE + rv * ROW_BYTES + (lane & 1) * 8;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            u32x2 lo, hi;
+            u32x4 vf;
             if constexpr (DL && FP8) {
-                oacc[mb] = mfma16x16x32(fp8x8_to_bf16x8(lds_read_tr8(vst + ((mb ^ swv) << 4))), pf, oacc[mb]);
-                continue;
-            } else if constexpr (DL) {
-                const int pos = ((2 * mb + ((lane & 3) >> 1)) ^ swv) << 4;
-                lo = lds_read_tr16(vst + pos);
-                hi = lds_read_tr16(vst + 16 * 256 + pos);
+                vf = fp8x8_to_bf16x8(lds_read_tr8(vst + ((mb ^ swv) << 4)));
             } else {
-                lo = lds_read_tr16(vt + mb * 16);
-                hi = lds_read_tr16(vt + 16 * VP + mb * 16);
+                u32x2 lo, hi;
+                if constexpr (DL) {
+                    const int pos = ((2 * mb + ((lane & 3) >> 1)) ^ swv) << 4;
+                    lo = lds_read_tr16(vst + pos);
+                    hi = lds_read_tr16(vst + 16 * ROW_BYTES + pos);
+                } else {
+                    lo = lds_read_tr16(vt + mb * 16);
+                    hi = lds_read_tr16(vt + 16 * VP + mb * 16);
+                }
+                vf = u32x4{lo.x, lo.y, hi.x, hi.y};
             }
-            oacc[mb] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pf, oacc[mb]);
+            oacc[mb] = mfma16x16x32(vf, pf, oacc[mb]);
         }
     }
 };
