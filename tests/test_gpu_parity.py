@@ -121,6 +121,8 @@ DECODE_CASES = [
     ([1] * 2, [300, 77], 8, 2, 256, 16),
     ([2, 3, 4, 1], [20, 0, 35, 64], 16, 4, 128, 16),   # short multi-token decode (4 x q_len <= 16 rows)
     ([1, 0, 1], [50, 10, 7], 32, 8, 128, 3),            # an empty request and a page size of 3
+    ([1], [20000], 8, 1, 128, 16),                      # one item over every wave: the chunked merge of ~600 partials
+    ([1, 1], [9000, 300], 16, 2, 128, 256),             # four items, one short: chunked merge, some items whole
 ]
 
 
