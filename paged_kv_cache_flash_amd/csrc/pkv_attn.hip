@@ -1664,14 +1664,12 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
 // wave_of(last tile) (those that own at least one tile); with one wave the
 // output is already final. The item comes from the block index, so the
 // metadata loads are independent of each other.
-// WIDE: for items covered by many waves (long contexts), partials are read
-// in chunks; with few partials per item the plain walk keeps the kernel small
-// and its occupancy high.
-template <bool WIDE>
+// CH: partials read per chunk: 16 for items covered by many waves (long
+// contexts), 4 otherwise (fewer registers, higher occupancy).
+template <int CH>
 __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
     const int lane = threadIdx.x & 63;
     const int hl = lane & 31;
-    const int base_lane = lane & 32;
     const int wgs = p.dec_rows >> 3;  // workgroups per item
     const int64_t item = blockIdx.x / wgs;
     const int r = (int)(item / p.Hkv);
@@ -1698,100 +1696,51 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
     const bool c0 = hl < nch, c1 = hl + 32 < nch;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 o0 = zero, o1 = zero;
-    float wsum = 0.f, Mu;
-    if constexpr (WIDE) {
-        // Partials in chunks of CH whose lse and output loads are issued
-        // together (they depend only on the slot), with a running maximum
-        // between chunks: about np / CH dependent round trips. Lane hl < CH
-        // of each half-wave reads the lse of partial j0 + hl (and decides
-        // whether it exists); the others take it by a lane shuffle.
-        constexpr int CH = 16;
-        float M = -INFINITY;
-        for (int j0 = 0; j0 < np; j0 += CH) {
-            const int jl = j0 + hl;
-            const float lsl = hl < CH && jl < np && owns_tiles(wf + jl)
-                                  ? p.part_lse[(slot0 + jl) * p.dec_rows + row16] : -INFINITY;
-            float ls[CH];
-            f32x4 v0[CH], v1[CH];
+    float wsum = 0.f;
+    // Partials in chunks of CH whose lse and output loads are issued
+    // together (they depend only on the slot), with a running maximum
+    // between chunks: about np / CH dependent round trips. Lane hl < CH
+    // of each half-wave reads the lse of partial j0 + hl (and decides
+    // whether it exists); the others take it by a lane shuffle.
+    float M = -INFINITY;
+    for (int j0 = 0; j0 < np; j0 += CH) {
+        const int jl = j0 + hl;
+        const float lsl = hl < CH && jl < np && owns_tiles(wf + jl)
+                              ? p.part_lse[(slot0 + jl) * p.dec_rows + row16] : -INFINITY;
+        float ls[CH];
+        f32x4 v0[CH], v1[CH];
 #pragma unroll
-            for (int u = 0; u < CH; ++u) {
-                ls[u] = __shfl(lsl, (lane & 32) + u);
-                v0[u] = zero;
-                v1[u] = zero;
-                if (j0 + u < np) {  // (np is the same for every lane of the wave)
-                    const float* src = p.part_o + ((slot0 + j0 + u) * p.dec_rows + row16) * p.hd;
-                    if (c0) v0[u] = *(const f32x4*)(src + 4 * hl);
-                    if (c1) v1[u] = *(const f32x4*)(src + 4 * (hl + 32));
-                }
-            }
-            float cm = M;
-#pragma unroll
-            for (int u = 0; u < CH; ++u) cm = fmaxf(cm, ls[u]);
-            if (cm == -INFINITY) continue;  // no partial yet
-            const float a = fast_exp2((M - cm) * kLog2e);  // 0 while nothing is accumulated
-            o0 *= a;
-            o1 *= a;
-            wsum *= a;
-            M = cm;
-#pragma unroll
-            for (int u = 0; u < CH; ++u) {
-                const float wj = fast_exp2((ls[u] - M) * kLog2e);  // 0 for absent partials
-                wsum += wj;
-                // an absent partial's slot holds stale bytes: select, never multiply by 0
-                if (wj != 0.f) {
-                    o0 += wj * v0[u];
-                    o1 += wj * v1[u];
-                }
+        for (int u = 0; u < CH; ++u) {
+            ls[u] = __shfl(lsl, (lane & 32) + u);
+            v0[u] = zero;
+            v1[u] = zero;
+            if (j0 + u < np) {  // (np is the same for every lane of the wave)
+                const float* src = p.part_o + ((slot0 + j0 + u) * p.dec_rows + row16) * p.hd;
+                if (c0) v0[u] = *(const f32x4*)(src + 4 * hl);
+                if (c1) v1[u] = *(const f32x4*)(src + 4 * (hl + 32));
             }
         }
-        Mu = M == -INFINITY ? 0.f : M;
-    } else {
-        float lsv[2];
-        float M = -INFINITY;
+        float cm = M;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int j = hl + 32 * c;
-            lsv[c] = (j < np && owns_tiles(wf + j)) ? p.part_lse[(slot0 + j) * p.dec_rows + row16] : -INFINITY;
-            M = fmaxf(M, lsv[c]);
-        }
-        for (int j = hl + 64; j < np; j += 32)
-            if (owns_tiles(wf + j)) M = fmaxf(M, p.part_lse[(slot0 + j) * p.dec_rows + row16]);
+        for (int u = 0; u < CH; ++u) cm = fmaxf(cm, ls[u]);
+        if (cm == -INFINITY) continue;  // no partial yet
+        const float a = fast_exp2((M - cm) * kLog2e);  // 0 while nothing is accumulated
+        o0 *= a;
+        o1 *= a;
+        wsum *= a;
+        M = cm;
 #pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        Mu = M == -INFINITY ? 0.f : M;
-        for (int j0 = 0; j0 < np; j0 += 32) {
-            const int j = j0 + hl;
-            float ls;
-            if (j0 < 64) ls = lsv[j0 >> 5];
-            else ls = (j < np && owns_tiles(wf + j)) ? p.part_lse[(slot0 + j) * p.dec_rows + row16] : -INFINITY;
-            const float wj = fast_exp2((ls - Mu) * kLog2e);  // 0 for absent partials
+        for (int u = 0; u < CH; ++u) {
+            const float wj = fast_exp2((ls[u] - M) * kLog2e);  // 0 for absent partials
             wsum += wj;
-            const int cnt = min(32, np - j0);
-            // four partials per step, their loads issued together
-            for (int k = 0; k < cnt; k += 4) {
-                f32x4 v0[4], v1[4];
-                float wk[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    wk[u] = __shfl(wj, base_lane + min(k + u, cnt - 1));
-                    if (k + u >= cnt) wk[u] = 0.f;
-                    const float* src = p.part_o + ((slot0 + j0 + min(k + u, cnt - 1)) * p.dec_rows + row16) * p.hd;
-                    v0[u] = c0 ? *(const f32x4*)(src + 4 * hl) : f32x4{0.f, 0.f, 0.f, 0.f};
-                    v1[u] = c1 ? *(const f32x4*)(src + 4 * (hl + 32)) : f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    // an absent partial's slot holds stale bytes: select, never multiply by 0
-                    if (wk[u] != 0.f) {
-                        o0 += wk[u] * v0[u];
-                        o1 += wk[u] * v1[u];
-                    }
-                }
+            // an absent partial's slot holds stale bytes: select, never multiply by 0
+            if (wj != 0.f) {
+                o0 += wj * v0[u];
+                o1 += wj * v1[u];
             }
         }
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
     }
+    const float Mu = M == -INFINITY ? 0.f : M;
     float inv, lse;
     finalize_row(Mu * kLog2e, wsum, sink_l2(p, h), 1.f, inv, lse);
     uint16_t* dst = (uint16_t*)p.out + (tok * p.H + h) * p.hd;
@@ -1913,10 +1862,10 @@ hipError_t launch_decode_balanced(const FwdParams& p, KvType kv, hipStream_t s) 
 hipError_t launch_combine_balanced(const FwdParams& p, hipStream_t s) {
     const int64_t items = (int64_t)p.B * p.Hkv;  // dec_rows / 8 workgroups per item
     const dim3 grid((unsigned)(items * (p.dec_rows / 8)));
-    // waves per item when all items are as long as the longest: the chunked
-    // merge pays off from about 16 partials per item
-    if (p.sk_waves >= 16 * items) hipLaunchKernelGGL(combine_balanced_kernel<true>, grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(combine_balanced_kernel<false>, grid, dim3(256), 0, s, p);
+    // waves per item when all items are as long as the longest: chunks of
+    // 16 partials pay off from about 16 partials per item
+    if (p.sk_waves >= 16 * items) hipLaunchKernelGGL(combine_balanced_kernel<16>, grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(combine_balanced_kernel<4>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
