@@ -413,6 +413,29 @@ def main():
     calls, main_ms, merge_ms = len(main_each), float(sum(main_each)), float(sum(merge_each))
     pkv.timing_enable(False)
 
+    # The cache write on its own: K calls captured in one HIP graph (a call
+    # launched eagerly is shorter than its host launch), timed with events
+    # around a replay, and its algorithmic bytes (new K and V read, written
+    # into the cache, and one int64 slot per token).
+    cache_write = None
+    if prob.paged and not args.eager:
+        cw_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cw_graph):
+            for i in range(args.steps):
+                kc, vc = reps[(args.warmup + i) % R]
+                pkv.pkv_cache_write(k_new, v_new, kc, vc, slots_new, ks, vs)
+        cw_graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cw_graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        cw_us = e0.elapsed_time(e1) * 1e3 / args.steps
+        cw_bytes = k_new.numel() * 2 * (k_new.element_size() + reps[0][0].element_size()) + slots_new.numel() * 8
+        cache_write = {"tokens": int(k_new.shape[0]), "us_per_call": round(cw_us, 2), "bytes": int(cw_bytes),
+                       "GB_per_s": round(cw_bytes / cw_us / 1e3, 1), "launch": "hip_graph"}
+        del cw_graph
+
     use_graph = not args.eager
     if use_graph:
         # The K timed steps captured into one HIP graph, as a serving engine
@@ -548,7 +571,7 @@ def main():
     line = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "fp8 QK^T, bf16 PV" if prob.q_dtype == "fp8" else "bf16", "data": "synthetic", "config": cfg, "roofline": roofline,
-            "cpu_baseline": cpu}
+            "cpu_baseline": cpu, "cache_write": cache_write}
     print(json.dumps(line), flush=True)
 
 
