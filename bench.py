@@ -8,10 +8,15 @@ the KV range is split, the log-sum-exp merge kernel). Inputs are resident in
 HBM before timing starts. The KV cache is replicated and the replicas are used
 in turn, so a step never finds its KV in the 256 MB last-level cache.
 
-Default workload (one GPU): paged decode, Llama-3-8B-like GQA (32 query / 8 kv
-heads, head size 128, bf16), batch 64, one query token per request, context
-lengths uniform in [512, 4096], page size 16, random block table. The metric is
-KV bytes read per second (GB/s) against the MI355X HBM peak of 8 TB/s.
+Default run (one GPU), the two halves of the headline metric in one process:
+paged decode, Llama-3-8B-like GQA (32 query / 8 kv heads, head size 128,
+bf16), batch 64, one query token per request, context lengths uniform in
+[512, 4096], page size 16, random block table, measured as KV bytes read per
+second (GB/s) against the MI355X HBM peak of 8 TB/s; and, nested under
+"prefill" in the same JSON line, chunked prefill (batch 8, new tokens uniform
+in [128, 2048] on cached contexts uniform in [0, 4096], same heads, page 16,
+causal) in TFLOP/s of visible query-key pairs against the 2.5 PFLOP/s bf16
+dense MFMA peak.
 Other workloads (--workload): chunked_prefill (TFLOP/s against the 2.5 PFLOP/s
 bf16 dense MFMA peak), long_decode, long_decode_cascade, fp8_decode,
 spec_decode (several new tokens per request; KV GB/s). The
@@ -177,10 +182,10 @@ def pmc_summary(args):
     copy_bytes = args.calibrate_bytes
     f_fac = copy_bytes / (1024 * mean_counter(cfetch_dir, "FETCH_SIZE", "copyBuffer"))
     w_fac = copy_bytes / (1024 * mean_counter(cwrite_dir, "WRITE_SIZE", "copyBuffer"))
-    kern = DOMINANT_KERNEL[args.workload]
+    kern = DOMINANT_KERNEL[args.workload or "paged_decode"]
     fetch = mean_counter(fetch_dir, "FETCH_SIZE", kern) * 1024 * f_fac
     write = mean_counter(write_dir, "WRITE_SIZE", kern) * 1024 * w_fac
-    print(f"{args.workload} {args.block_size} {kern} {int(round(fetch))} {int(round(write))} {kernel_sources_hash()}"
+    print(f"{args.workload or 'paged_decode'} {args.block_size} {kern} {int(round(fetch))} {int(round(write))} {kernel_sources_hash()}"
           f"  # copy factors fetch {f_fac:.4f} write {w_fac:.4f}")
 
 
@@ -252,59 +257,8 @@ def cascade_sweep():
         del reps
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="paged_decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--block-size", type=int, default=0,
-                    help="page size (default 16; a page as long as the longest request makes the KV contiguous)")
-    ap.add_argument("--batch", type=int, default=0, help="paged_decode: requests (default 64)")
-    ap.add_argument("--heads", type=int, default=0, help="paged_decode: query heads (default 32)")
-    ap.add_argument("--kv-heads", type=int, default=0, help="paged_decode: kv heads (default 8)")
-    ap.add_argument("--num-splits", type=int, default=0, help="0 = library's choice")
-    ap.add_argument("--sliding-window", type=int, default=0, help="a query sees at most this many keys (0: off)")
-    ap.add_argument("--softcap", type=float, default=0.0, help="logits soft cap (0: off)")
-    ap.add_argument("--sinks", action="store_true", help="one sink logit per query head (seeded)")
-    ap.add_argument("--alibi", action="store_true", help="ALiBi with the geometric slopes 2^(-8 (h + 1) / H)")
-    ap.add_argument("--replicas", type=int, default=0, help="KV cache copies used in turn (0 = enough for 1.5 GB)")
-    ap.add_argument("--eager", action="store_true",
-                    help="time eager launches only (default: the timed steps are one captured HIP graph)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
-    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="only summarise rocprofv3 --pmc output of this workload into a traffic line")
-    ap.add_argument("--calibrate-bytes", type=int, default=1 << 30, help="bytes of the copy in the calibration runs")
-    ap.add_argument("--cascade-sweep", action="store_true",
-                    help="only time plain against cascade decode on shared-prefix batches, next to the library's "
-                         "cascade choice (one JSON line per batch)")
-    args = ap.parse_args()
-
-    if args.pmc_summary:
-        pmc_summary(args)
-        return
-    if args.cascade_sweep:
-        cascade_sweep()
-        return
-    if args.calibrate_copy:
-        import torch
-        n = args.calibrate_copy << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}), flush=True)
-        return
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path (the attention shards by request "
-              "or kv head with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
+def run_one(args, wl):
+    """Time workload `wl` and return its result line (without printing it)."""
     import torch
 
     import paged_kv_cache_flash_amd as pkv
@@ -319,12 +273,12 @@ def main():
             return torch.from_numpy(a).to(dev).view(torch.float8_e4m3fn)
         return torch.from_numpy(a).to(dev)
     variants = args.sliding_window > 0 or args.softcap > 0 or args.sinks or args.alibi
-    if variants and args.workload == "long_decode_cascade":
+    if variants and wl == "long_decode_cascade":
         raise SystemExit("bench: the attention variants are not benchmarked on the cascade workload")
     t0 = time.time()
     over = {k: v for k, v in (("B", args.batch), ("H", args.heads), ("Hkv", args.kv_heads)) if v}
-    prob = make(args.workload, args.block_size, over)
-    log(f"[bench] workload {args.workload}: B={prob.B} T={prob.T} sumL={int(prob.seq_lens.sum())} "
+    prob = make(wl, args.block_size, over)
+    log(f"[bench] workload {wl}: B={prob.B} T={prob.T} sumL={int(prob.seq_lens.sum())} "
         f"H={prob.H} Hkv={prob.Hkv} hd={prob.hd} bs={prob.bs} cache={prob.cache_dtype} "
         f"(generated in {time.time() - t0:.1f}s)")
 
@@ -382,6 +336,9 @@ def main():
                                            prob.max_seqlen_k, prob.scale, prob.causal, args.num_splits, W)
     else:
         splits = None
+        ws = torch.empty(pkv.pkv_cascade_workspace_size(q, reps[0][0], reps[0][1], qsl, seq_lens, bt,
+                                                        prob.shared_prefix, prob.max_seqlen_q, prob.max_seqlen_k,
+                                                        prob.scale), dtype=torch.uint8, device=dev)
 
     def step(i):
         kc, vc = reps[i % R]
@@ -389,7 +346,7 @@ def main():
             pkv.pkv_cache_write(k_new, v_new, kc, vc, slots_new, ks, vs)
         if cascade:
             pkv.cascade_attention(q, kc, vc, qsl, seq_lens, bt, prob.shared_prefix, prob.max_seqlen_q,
-                                  prob.max_seqlen_k, prob.scale, k_scale=ks, v_scale=vs, out=out)
+                                  prob.max_seqlen_k, prob.scale, k_scale=ks, v_scale=vs, out=out, workspace=ws)
         else:
             pkv.pkv_varlen_fwd(q, kc, vc, qsl, seq_lens, bt, prob.max_seqlen_q, prob.max_seqlen_k, out=out,
                                lse=lse, num_splits=args.num_splits, workspace=ws, **fwd_kw)
@@ -456,34 +413,41 @@ def main():
         f"{ms_eager:.4f}); attention calls {calls}, main kernel {main_ms / max(calls, 1):.4f} ms avg, "
         f"merge {merge_ms / max(calls, 1):.4f} ms avg")
 
-    decode_like = args.workload not in PREFILL_WORKLOADS
+    decode_like = wl not in PREFILL_WORKLOADS
     # HBM bytes per launch of the dominant kernel from committed counter runs
     # (None unless they were taken on the current kernel sources)
-    traffic = None if variants else measured_traffic(args.workload, prob.bs)
+    traffic = None if variants else measured_traffic(wl, prob.bs)
     if decode_like:
         kvb = kv_bytes(prob, unique=cascade, window=W)
         value = kvb / (ms_step * 1e-3) / 1e9
         metric, unit = "paged decode KV GB/s", "GB/s"
-        # the dominant kernel is the attention kernel; per step it reads the
-        # whole KV once (cascade: a prefix launch and a suffix launch per step)
-        achieved = kvb / (main_ms / args.steps * 1e-3) / 1e9
+        # the attention reads the whole KV once per step (cascade: a prefix
+        # launch and a suffix launch per step); its time is the attention
+        # kernel plus the split-KV merge kernel, and the dominant kernel alone
+        # is reported beside it
+        achieved = kvb / ((main_ms + merge_ms) / args.steps * 1e-3) / 1e9
+        achieved_k = kvb / (main_ms / args.steps * 1e-3) / 1e9
         # every algorithmic byte: K/V, q, out, lse and the block-table entries read
         used_pages = int(((prob.seq_lens.astype(np.int64) + prob.bs - 1) // prob.bs).sum()) if prob.paged else 0
         all_bytes = kvb + prob.T * prob.H * prob.hd * 2 * (1 if prob.q_dtype == "fp8" else 2) \
             + prob.T * prob.H * prob.hd * 2 + prob.T * prob.H * 4 + used_pages * 4
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "timed": "attention kernel + split-KV merge kernel",
                     "algorithmic_bytes_per_launch": kvb,
                     "all_algorithmic_bytes_per_launch": int(all_bytes),
-                    "achieved_all_bytes": round(all_bytes / (main_ms / args.steps * 1e-3) / 1e9, 1)}
+                    "achieved_all_bytes": round(all_bytes / ((main_ms + merge_ms) / args.steps * 1e-3) / 1e9, 1),
+                    "kernel_only": {"kernel": DOMINANT_KERNEL[wl], "achieved": round(achieved_k, 1),
+                                    "frac": round(achieved_k / HBM_PEAK_GBS, 4)}}
     else:
         fl = visible_flops(prob, W)
         value = fl / (ms_step * 1e-3) / 1e12
         metric, unit = ("causal prefill TFLOP/s" if prob.causal else "non-causal attention TFLOP/s"), "TFLOP/s"
-        achieved = fl / (main_ms / args.steps * 1e-3) / 1e12
+        achieved = fl / ((main_ms + merge_ms) / args.steps * 1e-3) / 1e12
         peak = FP8_QK_BF16_PV_PEAK_TFLOPS if prob.q_dtype == "fp8" else BF16_PEAK_TFLOPS
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                    "timed": DOMINANT_KERNEL[wl] + (" + split-KV merge kernel" if merge_ms > 0 else ""),
                     "algorithmic_flops_per_launch": fl}
 
     cpu = None
@@ -511,8 +475,10 @@ def main():
                                         v_scale=prob.v_scale, q_scale=prob.q_scale, **var_o)
         tol = 5e-2 if prob.cache_dtype == "fp8" else 1e-2
         o = out.float().cpu().numpy().astype(np.float64)[sample]
+        # the bar is tol, widened by half a bf16 ulp only where that rounding
+        # of the exact answer alone exceeds tol (|ref| >= 4 at 1e-2)
         half_ulp = np.where(np.abs(ref) > 0, np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8), 0)
-        if not np.all(np.abs(o - ref) <= tol + half_ulp):
+        if not np.all(np.abs(o - ref) <= np.where(half_ulp > tol, tol + half_ulp, tol)):
             raise SystemExit(f"bench: sampled rows differ from the oracle by {np.abs(o - ref).max():.3e}")
         if not cascade:
             lerr = np.abs(lse.cpu().numpy()[:, sample] - ref_lse).max()
@@ -546,8 +512,8 @@ def main():
                          f"{t_cpu:.1f}s"}
         log(f"[bench] oracle: {cpu}")
 
-    desc = WORKLOADS[args.workload]
-    if over or (args.block_size and args.workload == "paged_decode"):
+    desc = WORKLOADS[wl]
+    if over or (args.block_size and wl == "paged_decode"):
         desc = (f"paged decode, {prob.H}/{prob.Hkv} heads, head {prob.hd}, bf16, batch {prob.B}, "
                 f"ctx U[512,4096], page {prob.bs}")
     if prob.bs != 16 and "page 16" in desc:
@@ -561,8 +527,10 @@ def main():
     if args.alibi:
         desc += ", ALiBi"
     med = float(np.median(main_each)) if main_each else None
+    roofline["kernel_ms_mean"] = round(main_ms / max(calls, 1), 5)
     roofline["kernel_ms_median"] = round(med, 5) if med else None
     roofline["kernel_ms_min"] = round(float(min(main_each)), 5) if main_each else None
+    roofline["merge_ms_mean"] = round(merge_ms / max(calls, 1), 5)
     cfg = {"workload": desc, "global_batch": prob.B, "seq_len": prob.max_seqlen_k,
            "num_heads": prob.H, "num_kv_heads": prob.Hkv, "head_size": prob.hd, "block_size": prob.bs if prob.paged else None,
            "kv_cache_dtype": prob.cache_dtype, "num_splits": splits, "cache_replicas": R,
@@ -572,6 +540,72 @@ def main():
             "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "fp8 QK^T, bf16 PV" if prob.q_dtype == "fp8" else "bf16", "data": "synthetic", "config": cfg, "roofline": roofline,
             "cpu_baseline": cpu, "cache_write": cache_write}
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
+                    help="one workload only (default: paged decode, with the chunked prefill leg nested)")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="page size (default 16; a page as long as the longest request makes the KV contiguous)")
+    ap.add_argument("--batch", type=int, default=0, help="paged_decode: requests (default 64)")
+    ap.add_argument("--heads", type=int, default=0, help="paged_decode: query heads (default 32)")
+    ap.add_argument("--kv-heads", type=int, default=0, help="paged_decode: kv heads (default 8)")
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--sliding-window", type=int, default=0, help="a query sees at most this many keys (0: off)")
+    ap.add_argument("--softcap", type=float, default=0.0, help="logits soft cap (0: off)")
+    ap.add_argument("--sinks", action="store_true", help="one sink logit per query head (seeded)")
+    ap.add_argument("--alibi", action="store_true", help="ALiBi with the geometric slopes 2^(-8 (h + 1) / H)")
+    ap.add_argument("--replicas", type=int, default=0, help="KV cache copies used in turn (0 = enough for 1.5 GB)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (default: the timed steps are one captured HIP graph)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="only summarise rocprofv3 --pmc output of this workload into a traffic line")
+    ap.add_argument("--calibrate-bytes", type=int, default=1 << 30, help="bytes of the copy in the calibration runs")
+    ap.add_argument("--cascade-sweep", action="store_true",
+                    help="only time plain against cascade decode on shared-prefix batches, next to the library's "
+                         "cascade choice (one JSON line per batch)")
+    args = ap.parse_args()
+
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    if args.cascade_sweep:
+        cascade_sweep()
+        return
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}), flush=True)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path (the attention shards by request "
+              "or kv head with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.workload is None:
+        # the headline pair: paged decode (KV GB/s against HBM) with the
+        # chunked prefill leg (TFLOP/s against bf16 MFMA) nested in its line
+        line = run_one(args, "paged_decode")
+        pre = run_one(args, "chunked_prefill")
+        line["prefill"] = {k: pre[k] for k in ("metric", "value", "unit", "ms_per_step", "higher_is_better",
+                                                "dtype", "config", "roofline", "cpu_baseline", "cache_write")}
+    else:
+        line = run_one(args, args.workload)
     print(json.dumps(line), flush=True)
 
 

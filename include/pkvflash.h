@@ -140,6 +140,9 @@ pkv_status pkv_cache_write(const void* key, const void* value, pkv_dtype src_dty
  *          product Q K^T runs on the fp8 matrix cores (exact products, fp32
  *          sums) and P V on the bf16 ones (P rounded to bf16), whatever the
  *          shape of the batch.
+ * Scales:  softmax_scale must be finite and > 0 (INVALID_ARG otherwise);
+ *          the device scalars k_scale, v_scale and q_scale must be finite
+ *          and > 0 (not checked: they live on the device).
  * Head size: a multiple of 8, at most 256 (the deep-dive page's backend rule).
  * Split-KV: num_splits 0 lets the library choose from the host sizes, 1 turns
  *          splitting off, > 1 asks for that many KV splits (at most 256). With
@@ -218,6 +221,39 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream);
 pkv_status pkv_merge_attn_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,
                                  const void* suffix_out, const float* suffix_lse, int64_t num_tokens,
                                  int32_t num_heads, int32_t head_size, pkv_dtype dtype, void* stream);
+
+/* ---------------------------------------------------------------- cascade
+ * Cascade attention (deep-dive page, cascade attention section): when every
+ * request of a batch begins with the same common_prefix_len KV tokens on the
+ * same pages, the batch runs as
+ *   1. a prefix pass: every query token of the batch against the shared
+ *      prefix (the first common_prefix_len / block_size pages of the first
+ *      block-table row), with no causal mask, as one request;
+ *   2. a suffix pass: each request against its own keys past the prefix (its
+ *      block-table row from page common_prefix_len / block_size on, KV length
+ *      seq_lens[r] - common_prefix_len), with the batch's mask;
+ *   3. pkv_merge_attn_states of the two states into a->out (and a->lse).
+ * The result equals pkv_varlen_fwd over the whole batch, with the shared
+ * pages read once instead of once per request.
+ * `a` describes the whole batch exactly as for pkv_varlen_fwd (block_table
+ * required); both passes and the merge run inside the library on `stream`.
+ * Preconditions (device data, not checked): every request's first
+ * common_prefix_len block-table entries are the same pages, and, with the
+ * causal mask, every request has at least common_prefix_len keys before its
+ * first query token (seq_lens[r] - q_len_r >= common_prefix_len), so each of
+ * its queries sees the whole prefix. Results are undefined otherwise (the
+ * kernels stay inside the pages the table names).
+ * Sinks (a->sinks) join the suffix pass only, so the merged normaliser counts
+ * them once. Not supported (UNSUPPORTED): ALiBi (its bias needs each query's
+ * own position, which the one-request prefix pass does not keep) and a
+ * sliding window (the deep-dive page's decision rules cascades out for it).
+ * Workspace: a->workspace must hold pkv_cascade_workspace_size(a, P) bytes
+ * (caller-owned): both passes' outputs and lse, and their split partials.
+ * common_prefix_len must be a positive multiple of block_size and at most
+ * max_seqlen_k (INVALID_ARG otherwise); WORKSPACE if the workspace is short.
+ * pkv_cascade_workspace_size returns 0 for arguments it rejects.            */
+size_t pkv_cascade_workspace_size(const pkv_varlen_args* a, int32_t common_prefix_len);
+pkv_status pkv_cascade_fwd(const pkv_varlen_args* a, int32_t common_prefix_len, void* stream);
 
 /* Whether to run a batch whose requests share their first common_prefix_len
  * KV tokens (the same pages) as a cascade: a prefix pass, a suffix pass and

@@ -69,7 +69,8 @@ class pkv_varlen_args(ctypes.Structure):
 
 
 EXPORTS = ("pkv_cache_write", "pkv_varlen_args_size", "pkv_varlen_check", "pkv_varlen_num_splits",
-           "pkv_varlen_workspace_size", "pkv_varlen_fwd", "pkv_merge_attn_states", "pkv_cascade_choose",
+           "pkv_varlen_workspace_size", "pkv_varlen_fwd", "pkv_merge_attn_states", "pkv_cascade_workspace_size",
+           "pkv_cascade_fwd", "pkv_cascade_choose",
            "pkv_last_error",
            "pkv_version", "pkv_timing_enable", "pkv_timing_collect", "pkv_timing_collect_calls")
 
@@ -99,6 +100,10 @@ def lib() -> ctypes.CDLL:
     L.pkv_varlen_fwd.argtypes = [ctypes.POINTER(pkv_varlen_args), vp]
     L.pkv_merge_attn_states.restype = i32
     L.pkv_merge_attn_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
+    L.pkv_cascade_workspace_size.restype = sz
+    L.pkv_cascade_workspace_size.argtypes = [ctypes.POINTER(pkv_varlen_args), i32]
+    L.pkv_cascade_fwd.restype = i32
+    L.pkv_cascade_fwd.argtypes = [ctypes.POINTER(pkv_varlen_args), i32, vp]
     L.pkv_cascade_choose.restype = i32
     L.pkv_cascade_choose.argtypes = [i32, i32, vp, i32, i32, i32, i32, vp, vp, vp]
     L.pkv_last_error.restype = ctypes.c_char_p
@@ -286,35 +291,51 @@ def use_cascade_attention(common_prefix_len, seq_lens, num_kv_heads, head_size, 
     return bool(use.value), tp.value, tc.value
 
 
+def pkv_cascade_workspace_size(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, common_prefix_len,
+                               max_seqlen_q, max_seqlen_k, softmax_scale, causal=True, softcap=0.0):
+    """Workspace bytes pkv_cascade_fwd needs for this batch (raises for arguments it rejects)."""
+    a = _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
+                     softmax_scale, causal, None, None, None, None, 0, None, 0, softcap)
+    n = int(lib().pkv_cascade_workspace_size(ctypes.byref(a), int(common_prefix_len)))
+    if n == 0:
+        _check(lib().pkv_varlen_check(ctypes.byref(a)))
+        raise PkvError(PKV_ERR_INVALID_ARG, lib().pkv_last_error().decode() or "cascade arguments rejected")
+    return n
+
+
+def pkv_cascade_fwd(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, common_prefix_len, max_seqlen_q,
+                    max_seqlen_k, softmax_scale, causal=True, out=None, lse=None, k_scale=None, v_scale=None,
+                    workspace=None, return_lse=False, stream=None, softcap=0.0, sinks=None, q_scale=None):
+    """Shared-prefix (cascade) attention in one library call: a prefix pass of every query over the
+    common prefix (the first common_prefix_len keys of the first block-table row, no mask), a suffix
+    pass of each request over its keys past the prefix, and the log-sum-exp merge (deep-dive page,
+    cascade attention section). Every request's first common_prefix_len / block_size pages must be the
+    same pages and, causal, precede its first query token. Sinks join the suffix pass only."""
+    T, H, hd = q.shape
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype,
+                          device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = pkv_cascade_workspace_size(q, k_cache, v_cache, query_start_loc, seq_lens, block_table,
+                                          common_prefix_len, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+                                          softcap)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
+                     softmax_scale, causal, out, lse, k_scale, v_scale, 0, workspace, 0, softcap, sinks, q_scale)
+    _check(lib().pkv_cascade_fwd(ctypes.byref(a), int(common_prefix_len), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
 def cascade_attention(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, common_prefix_len,
                       max_seqlen_q, max_seqlen_k, softmax_scale, k_scale=None, v_scale=None, out=None,
-                      return_lse=False, stream=None, softcap=0.0, sinks=None):
-    """Shared-prefix attention as three library calls (deep-dive page, cascade attention section):
-    every query against the common prefix (non-causal, first block-table row), each request against
-    its own suffix (causal, the block table past the prefix blocks), then the log-sum-exp merge.
-    common_prefix_len must be a multiple of the block size. A soft cap applies to both passes; sinks
-    enter the suffix pass only, so the merged normaliser counts them once."""
-    T, H, hd = q.shape
-    bs = k_cache.shape[1]
-    if common_prefix_len % bs:
-        raise ValueError("common_prefix_len must be a multiple of the block size")
-    dev = q.device
-    nblk = common_prefix_len // bs
-    # built on the device (no host copies), so the whole cascade can be captured in a HIP graph
-    prefix_qsl = torch.arange(2, dtype=torch.int32, device=dev) * T
-    prefix_len = torch.full((1,), common_prefix_len, dtype=torch.int32, device=dev)
-    o_p, l_p = pkv_varlen_fwd(q, k_cache, v_cache, prefix_qsl, prefix_len, block_table[:1], T, common_prefix_len,
-                              softmax_scale, causal=False, k_scale=k_scale, v_scale=v_scale, return_lse=True,
-                              stream=stream, softcap=softcap)
-    o_s, l_s = pkv_varlen_fwd(q, k_cache, v_cache, query_start_loc, seq_lens - common_prefix_len,
-                              block_table[:, nblk:], max_seqlen_q, max_seqlen_k - common_prefix_len, softmax_scale,
-                              causal=True, k_scale=k_scale, v_scale=v_scale, return_lse=True, stream=stream,
-                              softcap=softcap, sinks=sinks)
-    if out is None:
-        out = torch.empty_like(q)
-    lse = torch.empty((H, T), dtype=torch.float32, device=dev) if return_lse else None
-    pkv_merge_attn_states(out, lse, o_p, l_p, o_s, l_s, stream=stream)
-    return (out, lse) if return_lse else out
+                      return_lse=False, stream=None, softcap=0.0, sinks=None, workspace=None):
+    """Causal shared-prefix attention (pkv_cascade_fwd with the causal mask)."""
+    return pkv_cascade_fwd(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, common_prefix_len,
+                           max_seqlen_q, max_seqlen_k, softmax_scale, causal=True, out=out, k_scale=k_scale,
+                           v_scale=v_scale, workspace=workspace, return_lse=return_lse, stream=stream,
+                           softcap=softcap, sinks=sinks)
 
 
 def timing_enable(on: bool = True):

@@ -97,7 +97,8 @@ pkv_status validate_sizes(const pkv_varlen_args* a) {
     if (a->q_dtype == PKV_FP8_E4M3FN && (a->head_size != 128 || a->num_heads / a->num_kv_heads > kPrefillMaxGroup))
         return fail(PKV_ERR_UNSUPPORTED, "an fp8 q needs head_size 128 and a group of at most %d heads",
                     kPrefillMaxGroup);
-    if (!std::isfinite(a->softmax_scale)) return fail(PKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (!std::isfinite(a->softmax_scale) || !(a->softmax_scale > 0.f))
+        return fail(PKV_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
     if (a->sliding_window < 0) return fail(PKV_ERR_INVALID_ARG, "sliding_window must be >= 0 (0: no window)");
     if (!(a->softcap >= 0.f) || !std::isfinite(a->softcap))
         return fail(PKV_ERR_INVALID_ARG, "softcap must be finite and >= 0 (0: off)");
@@ -112,9 +113,13 @@ pkv_status validate_sizes(const pkv_varlen_args* a) {
         if (a->num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
         if (a->num_blocks * (int64_t)a->block_size >= (int64_t(1) << 31))
             return fail(PKV_ERR_UNSUPPORTED, "num_blocks * block_size must be < 2^31");
-        if (a->max_seqlen_k < a->max_seqlen_q)
+        // (causal: every request's KV includes its own new tokens; a
+        // non-causal pass, such as a cascade's prefix pass, may have more
+        // queries than keys)
+        if (a->causal && a->max_seqlen_k < a->max_seqlen_q)
             return fail(PKV_ERR_INVALID_ARG, "max_seqlen_k (%d) < max_seqlen_q (%d): seq_lens include the new tokens",
                         a->max_seqlen_k, a->max_seqlen_q);
+        if (a->max_seqlen_k < 0) return fail(PKV_ERR_INVALID_ARG, "max_seqlen_k must be >= 0");
         if (a->block_table_stride < cdiv(a->max_seqlen_k, a->block_size))
             return fail(PKV_ERR_INVALID_ARG, "block_table_stride %lld < ceil(max_seqlen_k / block_size) = %lld",
                         (long long)a->block_table_stride, (long long)cdiv(a->max_seqlen_k, a->block_size));
@@ -231,9 +236,19 @@ size_t pkv_varlen_workspace_size(const pkv_varlen_args* a) {
     return make_plan(a).workspace;
 }
 
-pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
-    pkv_status st = validate(a);
-    if (st != PKV_OK || a->num_tokens == 0) return st;
+}  // extern "C"
+
+namespace {
+
+// How one forward pass reads the batch's metadata (cascade passes; the
+// defaults are a plain forward).
+struct PassOpts {
+    int32_t single_len = 0;  // > 0: all tokens form one request with this KV length
+    int32_t seq_off = 0;     // keys before this index are another pass's
+};
+
+// One forward over validated arguments (a->workspace holds the partials).
+pkv_status run_fwd(const pkv_varlen_args* a, const PassOpts& o, hipStream_t s) {
     Plan pl = make_plan(a);
     if (pl.kind == Kind::DecodeBalanced && (a->workspace == nullptr || a->workspace_bytes < pl.workspace)) {
         // no room for the balanced schedule's partials: the other kernels,
@@ -250,7 +265,6 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
         pl.split_len = (int32_t)std::max<int64_t>(a->block_table ? a->max_seqlen_k : a->max_seqlen_q, 1);
         pl.workspace = 0;
     }
-    hipStream_t s = (hipStream_t)stream;
     FwdParams p{};
     p.q = a->q;
     p.k_cache = a->k_cache;
@@ -284,6 +298,8 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     p.softcap_inv2 = a->softcap > 0.f ? 2.f / a->softcap : 0.f;
     p.sinks = a->sinks;
     p.alibi = a->alibi_slopes;
+    p.single_len = o.single_len;
+    p.seq_off = o.seq_off;
     if (pl.kind == Kind::DecodeBalanced) {
         const int64_t slots = pl.splits + (int64_t)a->num_seqs * a->num_kv_heads;
         p.sk_waves = pl.splits;
@@ -326,6 +342,112 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
         g_tim.has_merge[g_tim.calls] = merge;
         ++g_tim.calls;
     }
+    return ok();
+}
+
+// ------------------------------------------------------------------ cascade
+
+// Round up to 256 bytes (each workspace region starts aligned).
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// The two passes of a cascade over the batch `a` with a shared prefix of P
+// keys, and where their results go in the workspace:
+// [prefix out][prefix lse][suffix out][suffix lse][the passes' own partials].
+struct Cascade {
+    pkv_varlen_args pre, suf;
+    PassOpts pre_o, suf_o;
+    size_t o_bytes, l_bytes, pass_ws, total;
+};
+
+pkv_status cascade_plan(const pkv_varlen_args* a, int32_t P, Cascade& c) {
+    if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+    if (!a->block_table) return fail(PKV_ERR_INVALID_ARG, "a cascade needs a paged cache (block_table)");
+    if (a->alibi_slopes)
+        return fail(PKV_ERR_UNSUPPORTED, "ALiBi needs each query's own position, which the prefix pass does not keep");
+    if (a->sliding_window > 0) return fail(PKV_ERR_UNSUPPORTED, "a cascade with a sliding window is not supported");
+    if (a->block_size <= 0 || P <= 0 || P % a->block_size != 0)
+        return fail(PKV_ERR_INVALID_ARG, "common_prefix_len %d must be a positive multiple of block_size %d", P,
+                    a->block_size);
+    if (P > a->max_seqlen_k)
+        return fail(PKV_ERR_INVALID_ARG, "common_prefix_len %d > max_seqlen_k %d", P, a->max_seqlen_k);
+    const int T = (int)a->num_tokens;
+    // prefix pass: every token against the P shared keys (the first row of
+    // the block table), as one request, not causal
+    c.pre = *a;
+    c.pre.num_seqs = 1;
+    c.pre.max_seqlen_q = T;
+    c.pre.max_seqlen_k = P;
+    c.pre.causal = 0;
+    c.pre.sinks = nullptr;  // the sink joins the suffix pass only
+    c.pre_o = PassOpts{};
+    c.pre_o.single_len = P;
+    // suffix pass: each request against its own keys past the prefix, with
+    // the block table from the first page after it
+    c.suf = *a;
+    c.suf.block_table = a->block_table + P / a->block_size;
+    c.suf.max_seqlen_k = a->max_seqlen_k - P;
+    c.suf_o = PassOpts{};
+    c.suf_o.seq_off = P;
+    pkv_status st = validate_sizes(&c.pre);
+    if (st != PKV_OK) return st;
+    st = validate_sizes(&c.suf);
+    if (st != PKV_OK) return st;
+    const size_t out_elt = a->q_dtype == PKV_F32 ? 4 : 2;
+    c.o_bytes = align256((size_t)a->num_tokens * a->num_heads * a->head_size * out_elt);
+    c.l_bytes = align256((size_t)a->num_tokens * a->num_heads * sizeof(float));
+    c.pass_ws = std::max(make_plan(&c.pre).workspace, make_plan(&c.suf).workspace);
+    c.total = 2 * (c.o_bytes + c.l_bytes) + c.pass_ws;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
+    pkv_status st = validate(a);
+    if (st != PKV_OK || a->num_tokens == 0) return st;
+    return run_fwd(a, PassOpts{}, (hipStream_t)stream);
+}
+
+size_t pkv_cascade_workspace_size(const pkv_varlen_args* a, int32_t common_prefix_len) {
+    if (validate_sizes(a) != PKV_OK || a->num_tokens == 0) return 0;
+    Cascade c;
+    if (cascade_plan(a, common_prefix_len, c) != PKV_OK) return 0;
+    return c.total;
+}
+
+pkv_status pkv_cascade_fwd(const pkv_varlen_args* a, int32_t common_prefix_len, void* stream) {
+    pkv_status st = validate(a);
+    if (st != PKV_OK || a->num_tokens == 0) return st;
+    Cascade c;
+    st = cascade_plan(a, common_prefix_len, c);
+    if (st != PKV_OK) return st;
+    if (!a->workspace || a->workspace_bytes < c.total)
+        return fail(PKV_ERR_WORKSPACE, "a cascade needs %zu workspace bytes, got %zu", c.total,
+                    a->workspace ? a->workspace_bytes : (size_t)0);
+    uint8_t* ws = (uint8_t*)a->workspace;
+    void* o_p = ws;
+    float* l_p = (float*)(ws + c.o_bytes);
+    void* o_s = ws + c.o_bytes + c.l_bytes;
+    float* l_s = (float*)(ws + 2 * c.o_bytes + c.l_bytes);
+    void* pass_ws = ws + 2 * (c.o_bytes + c.l_bytes);
+    hipStream_t s = (hipStream_t)stream;
+    c.pre.out = o_p;
+    c.pre.lse = l_p;
+    c.pre.workspace = pass_ws;
+    c.pre.workspace_bytes = c.pass_ws;
+    st = run_fwd(&c.pre, c.pre_o, s);
+    if (st != PKV_OK) return st;
+    c.suf.out = o_s;
+    c.suf.lse = l_s;
+    c.suf.workspace = pass_ws;
+    c.suf.workspace_bytes = c.pass_ws;
+    st = run_fwd(&c.suf, c.suf_o, s);
+    if (st != PKV_OK) return st;
+    const bool f32 = a->q_dtype == PKV_F32;
+    hipError_t e = launch_merge(a->out, a->lse, o_p, l_p, o_s, l_s, a->num_tokens, a->num_heads, a->head_size, f32, s);
+    if (e != hipSuccess) return hip_fail(e, "cascade merge launch");
     return ok();
 }
 

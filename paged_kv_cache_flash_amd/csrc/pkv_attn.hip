@@ -87,8 +87,10 @@ __device__ __forceinline__ u32x4 load_kv8(const void* base, int64_t elem) {
 }
 
 // Request owning packed token `tok` (binary search over query_start_loc).
-__device__ __forceinline__ int request_of(const int32_t* qsl, int B, int64_t tok) {
-    int lo = 0, hi = B - 1;
+__device__ __forceinline__ int request_of(const FwdParams& p, int64_t tok) {
+    if (p.single_len > 0) return 0;
+    const int32_t* qsl = p.qsl;
+    int lo = 0, hi = p.B - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (qsl[mid] <= tok) lo = mid; else hi = mid - 1;
@@ -135,18 +137,35 @@ __device__ __forceinline__ float sink_l2(const FwdParams& p, int h) {
 // (natural log). A sink logit (log2 domain; -inf: none) joins the normaliser
 // and adds no value: factor = vsc / (l + 2^(sink - m)), with both terms taken
 // against max(m, sink) so neither can overflow.
-__device__ __forceinline__ void finalize_row(float m, float l, float sink2, float vsc, float& factor, float& lse) {
+//
+// lc is the sum the accumulator's own weights add up to: where the
+// probabilities are rounded to bf16 for the P V product, the sum of those
+// rounded values, so that the output is a weighted mean of value rows whose
+// weights add up to one (for a row dominated by one key the output is then
+// that key's value row, however its weight was rounded). lse comes from the
+// sum of the unrounded probabilities, l.
+__device__ __forceinline__ void finalize_row(float m, float l, float lc, float sink2, float vsc, float& factor,
+                                             float& lse) {
     if (sink2 == -INFINITY) {
-        factor = l > 0.f ? vsc / l : 0.f;
+        factor = lc > 0.f ? vsc / lc : 0.f;
         const float mu = m == -INFINITY ? 0.f : m;
         lse = l > 0.f ? (mu + fast_log2(l)) * kLn2 : -INFINITY;
     } else {
         const float mu = fmaxf(m, sink2);
         const float a = l > 0.f ? fast_exp2(m - mu) : 0.f;
-        const float lt = l * a + fast_exp2(sink2 - mu);
-        factor = vsc * a / lt;
-        lse = (mu + fast_log2(lt)) * kLn2;
+        const float es = fast_exp2(sink2 - mu);
+        factor = vsc * a / (lc * a + es);
+        lse = (mu + fast_log2(l * a + es)) * kLn2;
     }
+}
+__device__ __forceinline__ void finalize_row(float m, float l, float sink2, float vsc, float& factor, float& lse) {
+    finalize_row(m, l, l, sink2, vsc, factor, lse);
+}
+
+// acc + the two bf16 values of a packed pair (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, 0x3F803F80u),
+                                           acc, false);
 }
 
 // ----------------------------------------------------------------- decode
@@ -261,13 +280,14 @@ struct DecodeTile {
     // soft cap (cap_l2 > 0) and the ALiBi bias (slope al2, query position
     // qpos),
     // online softmax, then O^T += V^T P^T with V^T read transposed. m_run is
-    // row-uniform (log2 domain), l_run per lane (this lane's keys only).
+    // row-uniform (log2 domain), l_run per lane (this lane's keys only), and
+    // lc_run the same sum over the probabilities as rounded to bf16 for PV.
     // (DL: the tile is in the global_load_lds layout above)
     template <bool VAR, bool DL = false>
     static __device__ __forceinline__ void compute(const uint16_t* stage, int lane, int t0, int lo, int limit,
                                                    float sl2, float cap_l2, float cap_inv2, float al2, int qpos,
                                                    const u32x4 (&qf)[KS], float& m_run, float& l_run,
-                                                   f32x4 (&oacc)[MB]) {
+                                                   float& lc_run, f32x4 (&oacc)[MB]) {
         const uint16_t* const kl = stage;
         const uint16_t* const vl = stage + K_ELEMS;
         const uint8_t* const st = (const uint8_t*)stage;
@@ -330,6 +350,7 @@ struct DecodeTile {
         // P^T as the B operand: k-slot 8*G + j holds key 16*(j/4) + 4*G + j%4
         const u32x4 pf = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]), pack_bf16x2(sv[4], sv[5]),
                           pack_bf16x2(sv[6], sv[7])};
+        lc_run = add_bf16_pair(pf.w, add_bf16_pair(pf.z, add_bf16_pair(pf.y, add_bf16_pair(pf.x, lc_run * alpha))));
         const uint16_t* vt = vl + (G * 4 + ((lane & 15) >> 2)) * VP + (lane & 3) * 4;
         // DL, bf16: row R (and R + 16), bytes 32 mb + 8 (lane & 3) onward:
         // chunk 2 mb + (lane & 3) / 2 at position chunk ^ dsw(R), half lane & 1.
@@ -413,7 +434,7 @@ __device__ __forceinline__ int decode_row_limit(const FwdParams& p, int lane, in
 template <int HD, bool FP8, bool PAGED, bool VAR>
 __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage, int lane, int r, int kh, int q0,
                                              int q_len, int L, int k_first, int step, int k_end, float& m_run,
-                                             float& l_run, f32x4 (&oacc)[HD / 16]) {
+                                             float& l_run, float& lc_run, f32x4 (&oacc)[HD / 16]) {
     using DT = DecodeTile<HD, FP8>;
     constexpr int NL = DT::NL;
     u32x4 qf[DT::KS];
@@ -428,6 +449,7 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage
 
     m_run = -INFINITY;
     l_run = 0.f;
+    lc_run = 0.f;
 #pragma unroll
     for (int i = 0; i < DT::MB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -478,7 +500,7 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage
             DT::load(p, lane, rows, kh, kr, vr);
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
             DT::template compute<VAR>(stage, lane, t_cur, lo, limit, sl2, p.softcap_l2, p.softcap_inv2, al2, qpos,
-                                      qf, m_run, l_run, oacc);
+                                      qf, m_run, l_run, lc_run, oacc);
             row_from(t_cur + 2 * step, pg, rows);
             t_cur += step;
             if (t_cur >= k_end) break;
@@ -486,9 +508,11 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // per-row sum over the four lane groups
+    // per-row sums over the four lane groups
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
+    lc_run += __shfl_xor(lc_run, 16);
+    lc_run += __shfl_xor(lc_run, 32);
 }
 
 // Split-KV decode: one workgroup per (KV split, kv head, request); its four
@@ -503,25 +527,25 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
     constexpr int VSM = NW * DecodeTile<HD, FP8>::ELEMS;  // bf16 elements of K/V staging
     constexpr int OSM = NW * 16 * HD * 2;           // the same bytes reused as fp32 partial outputs
     __shared__ __attribute__((aligned(16))) uint16_t smem[VSM > OSM ? VSM : OSM];
-    __shared__ float sm_m[NW][16], sm_l[NW][16];
+    __shared__ float sm_m[NW][16], sm_l[NW][16], sm_lc[NW][16];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
     const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
-    const int q0 = p.qsl[r];
-    const int q_len = p.qsl[r + 1] - q0;
+    const int q0 = req_q0(p, r);
+    const int q_len = req_qend(p, r) - q0;
     if (q_len <= 0) return;
-    const int L = p.seq_lens ? p.seq_lens[r] : q_len;
+    const int L = req_L(p, r, q_len);
     const int base = VAR ? window_base(p, q_len, L) : 0;
     const int k_begin = base + (p.num_splits > 1 ? s * p.split_len : 0);
     const int k_end = p.num_splits > 1 ? min(L, k_begin + p.split_len) : L;
     if (k_begin >= k_end) return;  // no row of this item sees a key here; the merge never reads it
 
-    float m_run, l_run;
+    float m_run, l_run, lc_run;
     f32x4 oacc[MB];
     decode_range<HD, FP8, PAGED, VAR>(p, smem + w * DecodeTile<HD, FP8>::ELEMS, lane, r, kh, q0, q_len, L, k_begin + w * TILE,
                                  NW * TILE,
-                                 k_end, m_run, l_run, oacc);
+                                 k_end, m_run, l_run, lc_run, oacc);
     const int row = lane & 15;
     const int G = lane >> 4;
     const int g = p.g;
@@ -533,6 +557,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
     if (lane < 16) {
         sm_m[w][lane] = m_run;
         sm_l[w][lane] = l_run;
+        sm_lc[w][lane] = lc_run;
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) *(f32x4*)(co + (w * 16 + row) * HD + mb * 16 + G * 4) = oacc[mb];
@@ -549,16 +574,17 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void decode_kernel(FwdParam
 #pragma unroll
     for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i][frow]);
     const float Mu = M == -INFINITY ? 0.f : M;
-    float wt[NW], Lt = 0.f;
+    float wt[NW], Lt = 0.f, Ltc = 0.f;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         wt[i] = fast_exp2(sm_m[i][frow] - Mu);
         Lt += wt[i] * sm_l[i][frow];
+        Ltc += wt[i] * sm_lc[i][frow];
     }
     // the sink joins the normaliser once, in the final output (split
     // partials leave it to the merge)
     float inv, lse;
-    finalize_row(M, Lt, p.num_splits == 1 ? sink_l2(p, head) : -INFINITY, vsc, inv, lse);
+    finalize_row(M, Lt, Ltc, p.num_splits == 1 ? sink_l2(p, head) : -INFINITY, vsc, inv, lse);
     float o[PER];
 #pragma unroll
     for (int d = 0; d < PER; ++d) {
@@ -601,8 +627,8 @@ __device__ __forceinline__ int decode_tiles_of(const FwdParams& p, int q_len, in
 }
 template <bool VAR>
 __device__ __forceinline__ int decode_tiles_of_request(const FwdParams& p, int r) {
-    const int ql = p.qsl[r + 1] - p.qsl[r];
-    return decode_tiles_of<VAR>(p, ql, p.seq_lens ? p.seq_lens[r] : ql);
+    const int ql = req_qend(p, r) - req_q0(p, r);
+    return decode_tiles_of<VAR>(p, ql, req_L(p, r, ql));
 }
 
 // Wave index whose tile range holds global tile t (ranges [w N / W, (w+1) N / W)).
@@ -685,9 +711,9 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
         if (wb < 0 || c.r >= wb + 64) {
             wb = c.r;
             const int x = wb + lane;
-            w_q0 = x < p.B ? p.qsl[x] : 0;
-            w_ql = x < p.B ? p.qsl[x + 1] - w_q0 : 0;
-            w_L = x < p.B ? (p.seq_lens ? p.seq_lens[x] : w_ql) : 0;
+            w_q0 = x < p.B ? req_q0(p, x) : 0;
+            w_ql = x < p.B ? req_qend(p, x) - w_q0 : 0;
+            w_L = x < p.B ? req_L(p, x, w_ql) : 0;
             w_n = decode_tiles_of<VAR>(p, w_ql, w_L);
             if constexpr (VAR) w_t0 = decode_first_tile<VAR>(p, w_ql, w_L);
         }
@@ -776,7 +802,7 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
     constexpr bool QN = RB == 1;
     u32x4 qf[RB][DT::KS], qn[DT::KS];
     int limit[RB], lo[RB], qpos[RB];
-    float sk[RB], sk_next[RB], m_run[RB], l_run[RB], al2[RB];
+    float sk[RB], sk_next[RB], m_run[RB], l_run[RB], lc_run[RB], al2[RB];
     f32x4 oacc[RB][MB];
     const bool has_sinks = p.sinks != nullptr;
     auto head_of = [&](int kh, int rb) { return kh * p.g + (16 * rb + row) % p.g; };
@@ -791,6 +817,7 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
         sk_next[rb] = -INFINITY;
         m_run[rb] = -INFINITY;
         l_run[rb] = 0.f;
+        lc_run[rb] = 0.f;
 #pragma unroll
         for (int i = 0; i < MB; ++i) oacc[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -812,13 +839,15 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
         w_whole = seg_t0 == 0 && c.t == c.n - 1;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            float l = l_run[rb];
+            float l = l_run[rb], lc = lc_run[rb];
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
+            lc += __shfl_xor(lc, 16);
+            lc += __shfl_xor(lc, 32);
             // a sink joins the normaliser once: in the final output of a
             // whole item, else in the merge
             float inv;
-            finalize_row(m_run[rb], l, w_whole ? sk[rb] : -INFINITY, vsc, inv, w_lse[rb]);
+            finalize_row(m_run[rb], l, lc, w_whole ? sk[rb] : -INFINITY, vsc, inv, w_lse[rb]);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) oacc[rb][mb] *= inv;
         }
@@ -849,6 +878,7 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
             }
             m_run[rb] = -INFINITY;
             l_run[rb] = 0.f;
+            lc_run[rb] = 0.f;
 #pragma unroll
             for (int i = 0; i < MB; ++i) oacc[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -897,7 +927,8 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
             if (rb == 0 || 16 * rb < c0.q_len * p.g)  // (a block without rows keeps its empty state)
                 DT::template compute<VAR, DMA>(DMA ? (const uint16_t*)(dstage + par * DT::DMA_STAGE) : stage, lane,
                                                c0.key0(), lo[rb], limit[rb], sl2, p.softcap_l2, p.softcap_inv2,
-                                               al2[rb], qpos[rb], qf[rb], m_run[rb], l_run[rb], oacc[rb]);
+                                               al2[rb], qpos[rb], qf[rb], m_run[rb], l_run[rb], lc_run[rb],
+                                               oacc[rb]);
         if (!c1.valid || c1_new) {
             close(c0);
             pending = true;
@@ -1065,12 +1096,12 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     const int r = rk / p.Hkv, kh = rk % p.Hkv;
     const int s = blockIdx.y;
     const int g = p.g;
-    const int q0 = p.qsl[r];
-    const int q_len = p.qsl[r + 1] - q0;
+    const int q0 = req_q0(p, r);
+    const int q_len = req_qend(p, r) - q0;
     const int tpw = ROWS / g;  // tokens per work item
     const int tok0 = qt * tpw;
     if (tok0 >= q_len) return;
-    const int L = p.seq_lens ? p.seq_lens[r] : q_len;
+    const int L = req_L(p, r, q_len);
     const int ctx = L - q_len;
     const int tok_last = min(q_len, tok0 + tpw) - 1;
     const int item_end = p.causal ? min(L, ctx + tok_last + 1) : L;
@@ -1244,7 +1275,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         }
     };
 
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY, l_run = 0.f, lc_run = 0.f;  // lc_run: sum of the bf16-rounded probabilities
     f32x16 oacc[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -1334,6 +1365,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
             const float m_new = fmaxf(m_run, m_tile);
             const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
             l_run *= alpha;
+            lc_run *= alpha;
 #pragma unroll
             for (int i = 0; i < MB; ++i) oacc[i] *= alpha;
             m_run = m_new;
@@ -1342,7 +1374,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     // probabilities of a tile as bf16 MFMA B operands, and their row sum
     auto expo = [&](f32x16 (&sacc)[KB], u32x4 (&pf)[2 * KB]) {
         const float nm = m_run == -INFINITY ? 0.f : -m_run;
-        float ps = 0.f;
+        float ps = 0.f, pc = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             float pv[16];
@@ -1352,11 +1384,15 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
                 ps += pv[e];
             }
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+            for (int hf = 0; hf < 2; ++hf) {
                 pf[2 * kb + hf] = u32x4{pack_bf16x2(pv[8 * hf + 0], pv[8 * hf + 1]), pack_bf16x2(pv[8 * hf + 2], pv[8 * hf + 3]),
                                         pack_bf16x2(pv[8 * hf + 4], pv[8 * hf + 5]), pack_bf16x2(pv[8 * hf + 6], pv[8 * hf + 7])};
+                const u32x4 w4 = pf[2 * kb + hf];
+                pc = add_bf16_pair(w4.w, add_bf16_pair(w4.z, add_bf16_pair(w4.y, add_bf16_pair(w4.x, pc))));
+            }
         }
         l_run += ps;
+        lc_run += pc;
     };
     // O^T += V^T P^T for one tile
     auto pv = [&](const uint8_t* vslot, const u32x4 (&pf)[2 * KB]) {
@@ -1464,9 +1500,10 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
 
     if (!row_ok) return;
     l_run += __shfl_xor(l_run, 32);
+    lc_run += __shfl_xor(lc_run, 32);
     // a sink joins the normaliser once, in the final output
     float inv, lse;
-    finalize_row(m_run, l_run, p.num_splits == 1 ? sink_l2(p, head) : -INFINITY, vsc, inv, lse);
+    finalize_row(m_run, l_run, lc_run, p.num_splits == 1 ? sink_l2(p, head) : -INFINITY, vsc, inv, lse);
     const int64_t tok = q0 + tl;
     if (p.num_splits == 1) {
         uint16_t* op = (uint16_t*)p.out + (tok * p.H + head) * HD + hsel * 4;
@@ -1506,11 +1543,11 @@ __global__ __launch_bounds__(64) void generic_kernel(FwdParams p) {
     const int lane = threadIdx.x;
     const int64_t tok = blockIdx.x;
     const int h = blockIdx.y, s = blockIdx.z;
-    const int r = request_of(p.qsl, p.B, tok);
-    const int q0 = p.qsl[r];
-    const int q_len = p.qsl[r + 1] - q0;
+    const int r = request_of(p, tok);
+    const int q0 = req_q0(p, r);
+    const int q_len = req_qend(p, r) - q0;
     const int t = (int)(tok - q0);
-    const int L = p.seq_lens ? p.seq_lens[r] : q_len;
+    const int L = req_L(p, r, q_len);
     const int n_vis = p.causal ? max(0, min(L, L - q_len + t + 1)) : L;
     const int k_split = window_base(p, q_len, L) + (p.num_splits > 1 ? s * p.split_len : 0);
     const int k_end = p.num_splits > 1 ? min(n_vis, k_split + p.split_len) : n_vis;
@@ -1604,10 +1641,10 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
     if (rowi >= p.T * p.H) return;  // whole half-waves leave together
     const int64_t tok = rowi / p.H;
     const int h = (int)(rowi % p.H);
-    const int r = request_of(p.qsl, p.B, tok);
-    const int q0 = p.qsl[r];
-    const int q_len = p.qsl[r + 1] - q0;
-    const int L = p.seq_lens ? p.seq_lens[r] : q_len;
+    const int r = request_of(p, tok);
+    const int q0 = req_q0(p, r);
+    const int q_len = req_qend(p, r) - q0;
+    const int L = req_L(p, r, q_len);
     const int t = (int)(tok - q0);
     const int n_vis = p.causal ? max(0, min(L, L - q_len + t + 1)) : L;
     const int base = window_base(p, q_len, L);
@@ -1675,10 +1712,10 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
     const int r = (int)(item / p.Hkv);
     const int kh = (int)(item % p.Hkv);
     const int row16 = (int)((blockIdx.x % wgs) * 8 + (threadIdx.x >> 5));  // row within the item
-    const int q0 = p.qsl[r];
-    const int q_len = p.qsl[r + 1] - q0;
+    const int q0 = req_q0(p, r);
+    const int q_len = req_qend(p, r) - q0;
     if (row16 >= q_len * p.g) return;  // whole half-waves leave together
-    const int L = p.seq_lens ? p.seq_lens[r] : q_len;
+    const int L = req_L(p, r, q_len);
     const int64_t N = (int64_t)p.Hkv * p.sk_prefix[p.B];
     const int64_t first = (int64_t)p.Hkv * p.sk_prefix[r];
     const int n_r = decode_tiles_of(p, q_len, L);

@@ -39,7 +39,24 @@ struct FwdParams {
     float softcap_inv2;       // 2 / softcap (soft cap on)
     const float* sinks;       // [H] natural-log sink logits, or nullptr
     const float* alibi;       // [H] ALiBi slopes, or nullptr
+    // cascade passes
+    int32_t single_len;       // > 0: the batch is one request of all T tokens with this KV
+                              // length (qsl and seq_lens are not read; B == 1)
+    int32_t seq_off;          // keys before this index belong to another pass: request r's
+                              // KV length is max(0, seq_lens[r] - seq_off), and the block
+                              // table passed in starts at that key's page
 };
+
+// Request metadata as every kernel reads it (cascade passes included).
+__device__ __forceinline__ int req_q0(const FwdParams& p, int r) { return p.single_len > 0 ? 0 : p.qsl[r]; }
+__device__ __forceinline__ int req_qend(const FwdParams& p, int r) {
+    return p.single_len > 0 ? (int)p.T : p.qsl[r + 1];
+}
+// KV length of request r with q_len query tokens (q_len itself in the flat layout).
+__device__ __forceinline__ int req_L(const FwdParams& p, int r, int q_len) {
+    if (p.single_len > 0) return p.single_len;
+    return p.seq_lens ? max(0, p.seq_lens[r] - p.seq_off) : q_len;
+}
 
 enum class KvType { BF16, FP8, F32 };
 

@@ -87,6 +87,9 @@ def test_valid_args_pass():
     (dict(num_splits=-1), pkv.PKV_ERR_INVALID_ARG),
     (dict(num_splits=300), pkv.PKV_ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), pkv.PKV_ERR_INVALID_ARG),     # the kernels need a positive scale
+    (dict(softmax_scale=-0.088), pkv.PKV_ERR_INVALID_ARG),
+    (dict(max_seqlen_k=100, max_seqlen_q=200, num_tokens=200, num_seqs=1), pkv.PKV_ERR_INVALID_ARG),  # causal
     (dict(sliding_window=-1), pkv.PKV_ERR_INVALID_ARG),
     (dict(q_dtype=pkv.PKV_FP8_E4M3FN, kv_dtype=pkv.PKV_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE),
      pkv.PKV_ERR_INVALID_ARG),  # fp8 q without q_scale
@@ -104,6 +107,52 @@ def test_invalid_args_rejected(kw, status):
     assert pkv.lib().pkv_last_error().decode() != ""
     # the forward rejects the same arguments before launching anything
     assert pkv.lib().pkv_varlen_fwd(ctypes.byref(a), None) == status
+
+
+def test_non_causal_may_have_more_queries_than_keys():
+    # a cascade's prefix pass: every token of the batch (1000) against a
+    # 256-key shared prefix, not causal
+    a = good_args(num_tokens=1000, num_seqs=1, max_seqlen_q=1000, max_seqlen_k=256, causal=0)
+    assert check(a) == pkv.PKV_OK
+    a.causal = 1
+    assert check(a) == pkv.PKV_ERR_INVALID_ARG
+
+
+def cascade_args(**kw):
+    """A chunked prefill of 1000 tokens over 4 requests sharing 256 keys."""
+    base = dict(num_tokens=1000, num_seqs=4, max_seqlen_q=400, max_seqlen_k=2048, block_table_stride=128)
+    base.update(kw)
+    return good_args(**base)
+
+
+def test_cascade_workspace_size():
+    L = pkv.lib()
+    a = cascade_args()
+    n = L.pkv_cascade_workspace_size(ctypes.byref(a), 256)
+    # two outputs (bf16) and two lse, each region 256-byte aligned, and at least
+    # nothing more for the passes' partials
+    o = (1000 * 32 * 128 * 2 + 255) // 256 * 256
+    l_ = (1000 * 32 * 4 + 255) // 256 * 256
+    assert n >= 2 * (o + l_)
+    # the whole batch alone, without a prefix
+    assert L.pkv_cascade_workspace_size(ctypes.byref(a), 0) == 0
+
+
+@pytest.mark.parametrize("P,kw,status", [
+    (0, {}, pkv.PKV_ERR_INVALID_ARG),                       # no prefix
+    (100, {}, pkv.PKV_ERR_INVALID_ARG),                     # not a multiple of the page size
+    (4096, {}, pkv.PKV_ERR_INVALID_ARG),                    # longer than max_seqlen_k
+    (256, dict(block_table=None, seq_lens=None), pkv.PKV_ERR_INVALID_ARG),  # flat K/V: nothing is shared
+    (256, dict(alibi_slopes=FAKE), pkv.PKV_ERR_UNSUPPORTED),
+    (256, dict(sliding_window=512), pkv.PKV_ERR_UNSUPPORTED),
+    (256, dict(softmax_scale=0.0), pkv.PKV_ERR_INVALID_ARG),
+    (256, {}, pkv.PKV_ERR_WORKSPACE),                       # no workspace
+    (256, dict(workspace=FAKE, workspace_bytes=1024), pkv.PKV_ERR_WORKSPACE),
+])
+def test_cascade_rejections(P, kw, status):
+    a = cascade_args(**kw)
+    assert pkv.lib().pkv_cascade_fwd(ctypes.byref(a), P, None) == status
+    assert pkv.lib().pkv_last_error().decode() != ""
 
 
 def test_null_args_pointer():

@@ -2,10 +2,12 @@
 configuration bench.py times (automatic split choice, cache written by
 pkv_cache_write, then one varlen forward).
 
-The float64 oracle evaluates sampled query rows one by one (every row for the
-long-context decode). Properties that hold at any size are checked on every
-row: outputs and lse finite, and every output element inside the range of
-the values it averages (|out| <= max |V|).
+The float64 oracle evaluates every query row of every workload, except the
+encoder, where all rows would take the oracle about five minutes (1.7e12
+float64 flops): there every row of the four shortest requests and every 16th
+row of the others are checked. Properties that hold at any size are checked on every row as well:
+outputs and lse finite, and every output element inside the range of the
+values it averages (|out| <= max |V|).
 
 Workloads (seeded, synthetic; the recipes are in workloads/):
   * paged decode: batch 64, context U[512, 4096], 32/8 heads, head 128, bf16, page 16
@@ -56,6 +58,10 @@ def check_whole_output(prob, out, lse):
     assert np.abs(o).max() <= vmax * (1 + slack) + 1e-6, "output outside the range of V"
 
 
+def all_rows(prob):
+    return np.arange(prob.T, dtype=np.int64)
+
+
 def run_full(prob, rows, out_tol, what):
     g = GpuProblem(prob, write_new_separately=True)
     out, lse = g.run(num_splits=0)
@@ -67,12 +73,12 @@ def run_full(prob, rows, out_tol, what):
 
 def test_full_paged_decode():
     prob = workloads.paged_decode()
-    run_full(prob, sample_rows(prob, 24, 1), BF16_OUT, "paged decode b64 bs16")
+    run_full(prob, all_rows(prob), BF16_OUT, "paged decode b64 bs16")
 
 
 def test_full_chunked_prefill():
     prob = workloads.chunked_prefill()
-    run_full(prob, sample_rows(prob, 48, 2), BF16_OUT, "chunked prefill b8")
+    run_full(prob, all_rows(prob), BF16_OUT, "chunked prefill b8")
 
 
 def test_full_long_decode():
@@ -99,7 +105,12 @@ def test_full_encoder():
     out, lse = g.run(num_splits=0)
     torch.cuda.synchronize()
     check_whole_output(prob, out, lse)
-    rows = sample_rows(prob, 24, 4)
+    # every row of the four shortest requests, every 16th row of the others
+    q_lens = np.diff(prob.query_start_loc)
+    whole = set(np.argsort(q_lens, kind="stable")[:4].tolist())
+    rows = np.concatenate([np.arange(prob.query_start_loc[r], prob.query_start_loc[r + 1])
+                           if r in whole else np.arange(prob.query_start_loc[r], prob.query_start_loc[r + 1], 16)
+                           for r in range(prob.B)]).astype(np.int64)
     ref, ref_lse = oracle_attention(prob, rows=rows)
     assert_parity(out, lse, ref, ref_lse, BF16_OUT, BF16_LSE, rows=rows, what="encoder")
 
@@ -112,7 +123,7 @@ def fp8_batch():
 @pytest.mark.parametrize("bs", [1, 8, 16, 64, 256])
 def test_full_fp8_decode_page_sweep(fp8_batch, bs):
     prob = workloads.with_page_size(fp8_batch, bs, seed=5 * 1000 + 1)
-    rows = sample_rows(prob, 16, 3)
+    rows = all_rows(prob)
     g = GpuProblem(prob, write_new_separately=True)
     out, lse = g.run(num_splits=0)
     torch.cuda.synchronize()
@@ -123,14 +134,14 @@ def test_full_fp8_decode_page_sweep(fp8_batch, bs):
 
 def test_full_spec_decode():
     prob = workloads.spec_decode(bs=16)
-    run_full(prob, sample_rows(prob, 32, 6), BF16_OUT, "multi-token decode")
+    run_full(prob, all_rows(prob), BF16_OUT, "multi-token decode")
 
 
 def test_full_fp8kv_prefill():
     prob = workloads.chunked_prefill(bs=16, cache_dtype="fp8")
-    run_full(prob, sample_rows(prob, 24, 7), FP8_OUT, "chunked prefill, fp8 cache")
+    run_full(prob, all_rows(prob), FP8_OUT, "chunked prefill, fp8 cache")
 
 
 def test_full_fp8q_prefill():
     prob = workloads.chunked_prefill(bs=16, cache_dtype="fp8", q_dtype="fp8")
-    run_full(prob, sample_rows(prob, 24, 8), FP8_OUT, "chunked prefill, fp8 q and cache")
+    run_full(prob, all_rows(prob), FP8_OUT, "chunked prefill, fp8 q and cache")

@@ -264,6 +264,21 @@ def test_cascade_equals_full_attention():
     assert_parity(out, lse, ref, ref_lse, BF16_OUT, BF16_LSE, what="cascade")
 
 
+@pytest.mark.parametrize("bs", [16, 64])
+def test_cascade_prefill_more_tokens_than_prefix(bs):
+    """A chunked prefill whose 651 new tokens share a 256-key prefix: the
+    prefix pass has more queries than keys and runs on the prefill kernel."""
+    prob = workloads.make_problem(608, [200, 300, 150, 1], [300, 256, 400, 700], H=32, Hkv=8, hd=128, bs=bs,
+                                  shared_prefix=256)
+    assert prob.T > prob.shared_prefix
+    g = GpuProblem(prob)
+    out, lse = pkv.cascade_attention(g.q, g.kc, g.vc, g.qsl, g.seq_lens, g.bt, prob.shared_prefix,
+                                     prob.max_seqlen_q, prob.max_seqlen_k, prob.scale, return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_attention(prob)
+    assert_parity(out, lse, ref, ref_lse, BF16_OUT, BF16_LSE, what=f"cascade prefill bs={bs}")
+
+
 def test_merge_attn_states_parity():
     rng = np.random.default_rng(605)
     T, H, hd = 33, 8, 128
