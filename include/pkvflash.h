@@ -208,6 +208,21 @@ size_t pkv_varlen_workspace_size(const pkv_varlen_args* a);
 
 pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as pkv_varlen_fwd, same plan and kernels, with its split-KV partials
+ * in a static device array of 64 MiB (67108864 bytes) inside the library
+ * instead of a->workspace (ignored). Each GPU the library runs on holds its
+ * own copy of the array until the process ends; its address is looked up on
+ * the first call on each device (with that device current). The call
+ * allocates nothing. Every call on a GPU shares that GPU's array and leaves
+ * its partials there: calls that overlap on one GPU (several streams, several
+ * threads) race and give undefined results. No kernel needs the array
+ * cleared. Errors: as pkv_varlen_fwd, and WORKSPACE when the plan's partials
+ * need more than the array holds (pkv_varlen_workspace_size(a) bytes; with
+ * num_splits = 1 none are needed).                                          */
+pkv_status pkv_varlen_fwd_noalloc(const pkv_varlen_args* a, void* stream);
+
 /* ----------------------------------------------------------------------- merge
  * Merge two attention states of the same queries (cascade attention: a state
  * over the shared prefix and one over each request's own suffix):

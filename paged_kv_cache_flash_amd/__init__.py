@@ -69,7 +69,8 @@ class pkv_varlen_args(ctypes.Structure):
 
 
 EXPORTS = ("pkv_cache_write", "pkv_varlen_args_size", "pkv_varlen_check", "pkv_varlen_num_splits",
-           "pkv_varlen_workspace_size", "pkv_varlen_fwd", "pkv_merge_attn_states", "pkv_cascade_workspace_size",
+           "pkv_varlen_workspace_size", "pkv_varlen_fwd", "pkv_varlen_fwd_noalloc", "pkv_merge_attn_states",
+           "pkv_cascade_workspace_size",
            "pkv_cascade_fwd", "pkv_cascade_choose",
            "pkv_last_error",
            "pkv_version", "pkv_timing_enable", "pkv_timing_collect", "pkv_timing_collect_calls")
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_varlen_workspace_size.argtypes = [ctypes.POINTER(pkv_varlen_args)]
     L.pkv_varlen_fwd.restype = i32
     L.pkv_varlen_fwd.argtypes = [ctypes.POINTER(pkv_varlen_args), vp]
+    L.pkv_varlen_fwd_noalloc.restype = i32
+    L.pkv_varlen_fwd_noalloc.argtypes = [ctypes.POINTER(pkv_varlen_args), vp]
     L.pkv_merge_attn_states.restype = i32
     L.pkv_merge_attn_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
     L.pkv_cascade_workspace_size.restype = sz
@@ -265,6 +268,19 @@ def pkv_varlen_fwd(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, 
                      sinks, q_scale, alibi_slopes)
     _check(lib().pkv_varlen_fwd(ctypes.byref(a), _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+def pkv_varlen_fwd_noalloc(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q,
+                           max_seqlen_k, softmax_scale, out, lse=None, causal=True, k_scale=None, v_scale=None,
+                           num_splits=0, stream=None, sliding_window=0, softcap=0.0, sinks=None, q_scale=None,
+                           alibi_slopes=None):
+    """pkv_varlen_fwd with its split-KV partials in the library's static device scratch: the call
+    allocates nothing (out, and lse if wanted, are the caller's). Calls that overlap on one GPU race."""
+    a = _varlen_args(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, max_seqlen_q, max_seqlen_k,
+                     softmax_scale, causal, out, lse, k_scale, v_scale, num_splits, None, sliding_window, softcap,
+                     sinks, q_scale, alibi_slopes)
+    _check(lib().pkv_varlen_fwd_noalloc(ctypes.byref(a), _stream(stream)))
+    return out
 
 
 def pkv_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse, stream=None):

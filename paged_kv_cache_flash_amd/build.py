@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkvflash.so")
 ARCH = "gfx950"
-SOURCES = ["pkv_attn.hip", "pkv_cache.hip", "pkv_api.cpp"]
+SOURCES = ["pkv_attn.hip", "pkv_cache.hip", "pkv_noalloc.hip", "pkv_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

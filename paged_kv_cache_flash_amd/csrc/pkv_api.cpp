@@ -410,6 +410,24 @@ pkv_status pkv_varlen_fwd(const pkv_varlen_args* a, void* stream) {
     return run_fwd(a, PassOpts{}, (hipStream_t)stream);
 }
 
+pkv_status pkv_varlen_fwd_noalloc(const pkv_varlen_args* a, void* stream) {
+    pkv_status st = validate(a);
+    if (st != PKV_OK || a->num_tokens == 0) return st;
+    // the plan is the one pkv_varlen_fwd makes; its partials must fit the scratch
+    const size_t need = make_plan(a).workspace;
+    if (need > kScratchBytes)
+        return fail(PKV_ERR_WORKSPACE,
+                    "this forward needs %zu bytes of split-KV scratch; the static scratch holds %zu "
+                    "(num_splits = 1 needs none)", need, kScratchBytes);
+    void* ptr = nullptr;
+    hipError_t e = scratch_for_current_device(&ptr);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    pkv_varlen_args b = *a;
+    b.workspace = ptr;
+    b.workspace_bytes = kScratchBytes;
+    return run_fwd(&b, PassOpts{}, (hipStream_t)stream);
+}
+
 size_t pkv_cascade_workspace_size(const pkv_varlen_args* a, int32_t common_prefix_len) {
     if (validate_sizes(a) != PKV_OK || a->num_tokens == 0) return 0;
     Cascade c;

@@ -60,6 +60,12 @@ __device__ __forceinline__ int req_L(const FwdParams& p, int r, int q_len) {
 
 enum class KvType { BF16, FP8, F32 };
 
+// Bytes of the device-resident scratch array behind pkv_varlen_fwd_noalloc
+// (one per GPU, held until the process ends), and its device address on the
+// current device (looked up on the first call per device).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_for_current_device(void** ptr);
+
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_decode(const FwdParams& p, KvType kv, hipStream_t s);
 hipError_t launch_decode_balanced(const FwdParams& p, KvType kv, hipStream_t s);
