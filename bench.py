@@ -53,7 +53,7 @@ PREFILL_WORKLOADS = ("chunked_prefill", "fp8kv_prefill", "fp8_prefill", "encoder
 # device copy of known size; each entry carries the hash of the kernel sources
 # it was taken on and is ignored once those sources change.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
-KERNEL_SOURCES = ["pkv_attn.hip", "pkv_device.h", "pkv_kernels.h"]
+KERNEL_SOURCES = ["pkv_attn.hip", "pkv_common.h", "pkv_device.h", "pkv_kernels.h"]
 DOMINANT_KERNEL = {"paged_decode": "decode_balanced_kernel", "chunked_prefill": "prefill_kernel",
                    "long_decode": "decode_balanced_kernel", "long_decode_cascade": "decode_balanced_kernel",
                    "fp8_decode": "decode_balanced_kernel", "spec_decode": "prefill_kernel",
