@@ -245,11 +245,17 @@ namespace {
 struct PassOpts {
     int32_t single_len = 0;  // > 0: all tokens form one request with this KV length
     int32_t seq_off = 0;     // keys before this index are another pass's
+    int32_t casc_len = 0;    // > 0: both cascade passes as one balanced decode (request 0 of
+                             // a->num_seqs is the shared prefix of this many keys)
 };
 
 // One forward over validated arguments (a->workspace holds the partials).
 pkv_status run_fwd(const pkv_varlen_args* a, const PassOpts& o, hipStream_t s) {
     Plan pl = make_plan(a);
+    if (o.casc_len > 0 && (pl.kind != Kind::DecodeBalanced || a->workspace == nullptr ||
+                           a->workspace_bytes < pl.workspace))
+        return fail(PKV_ERR_WORKSPACE, "the one-launch cascade needs the balanced decode and %zu workspace bytes",
+                    pl.workspace);
     if (pl.kind == Kind::DecodeBalanced && (a->workspace == nullptr || a->workspace_bytes < pl.workspace)) {
         // no room for the balanced schedule's partials: the other kernels,
         // unsplit unless their partials fit
@@ -300,6 +306,7 @@ pkv_status run_fwd(const pkv_varlen_args* a, const PassOpts& o, hipStream_t s) {
     p.alibi = a->alibi_slopes;
     p.single_len = o.single_len;
     p.seq_off = o.seq_off;
+    p.casc_len = o.casc_len;
     if (pl.kind == Kind::DecodeBalanced) {
         const int64_t slots = pl.splits + (int64_t)a->num_seqs * a->num_kv_heads;
         p.sk_waves = pl.splits;
@@ -334,7 +341,9 @@ pkv_status run_fwd(const pkv_varlen_args* a, const PassOpts& o, hipStream_t s) {
     const bool merge = pl.kind == Kind::DecodeBalanced || pl.splits > 1;
     if (merge) {
         if (timed) (void)hipEventRecord(ev[2], s);
-        e = pl.kind == Kind::DecodeBalanced ? launch_combine_balanced(p, s) : launch_combine(p, a->q_dtype == PKV_F32, s);
+        e = pl.kind != Kind::DecodeBalanced ? launch_combine(p, a->q_dtype == PKV_F32, s)
+            : o.casc_len > 0              ? launch_combine_cascade(p, s)
+                                          : launch_combine_balanced(p, s);
         if (e != hipSuccess) return hip_fail(e, "split merge kernel launch");
         if (timed) (void)hipEventRecord(ev[3], s);
     }
@@ -357,6 +366,11 @@ struct Cascade {
     pkv_varlen_args pre, suf;
     PassOpts pre_o, suf_o;
     size_t o_bytes, l_bytes, pass_ws, total;
+    // one launch: the batch as a balanced decode with the shared prefix as
+    // request 0 (every token of the batch against it, no causal mask)
+    bool fused;
+    pkv_varlen_args one;
+    PassOpts one_o;
 };
 
 pkv_status cascade_plan(const pkv_varlen_args* a, int32_t P, Cascade& c) {
@@ -397,6 +411,21 @@ pkv_status cascade_plan(const pkv_varlen_args* a, int32_t P, Cascade& c) {
     c.l_bytes = align256((size_t)a->num_tokens * a->num_heads * sizeof(float));
     c.pass_ws = std::max(make_plan(&c.pre).workspace, make_plan(&c.suf).workspace);
     c.total = 2 * (c.o_bytes + c.l_bytes) + c.pass_ws;
+    // The one-launch form, when the batch is decode-shaped: all of its query
+    // rows (every token x the group) fit one item of the balanced decode.
+    c.fused = false;
+    c.one = *a;
+    c.one.num_seqs = a->num_seqs + 1;
+    c.one.max_seqlen_q = T;
+    c.one_o = PassOpts{};
+    c.one_o.casc_len = P;
+    if (a->num_splits == 0 && validate_sizes(&c.one) == PKV_OK) {
+        const Plan pl = make_plan(&c.one);
+        if (pl.kind == Kind::DecodeBalanced) {
+            c.fused = true;
+            c.total = pl.workspace;
+        }
+    }
     return ok();
 }
 
@@ -444,6 +473,11 @@ pkv_status pkv_cascade_fwd(const pkv_varlen_args* a, int32_t common_prefix_len, 
     if (!a->workspace || a->workspace_bytes < c.total)
         return fail(PKV_ERR_WORKSPACE, "a cascade needs %zu workspace bytes, got %zu", c.total,
                     a->workspace ? a->workspace_bytes : (size_t)0);
+    if (c.fused) {  // both passes and the merge: one decode launch, one merge launch
+        c.one.workspace = a->workspace;
+        c.one.workspace_bytes = a->workspace_bytes;
+        return run_fwd(&c.one, c.one_o, (hipStream_t)stream);
+    }
     uint8_t* ws = (uint8_t*)a->workspace;
     void* o_p = ws;
     float* l_p = (float*)(ws + c.o_bytes);

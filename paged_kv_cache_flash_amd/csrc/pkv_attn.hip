@@ -273,10 +273,11 @@ __device__ __forceinline__ float decode_row_alibi(const FwdParams& p, int lane, 
 }
 
 // Largest key index + 1 that query row row0 + lane % 16 of an item may see.
-__device__ __forceinline__ int decode_row_limit(const FwdParams& p, int lane, int q_len, int L, int row0 = 0) {
+__device__ __forceinline__ int decode_row_limit(const FwdParams& p, int lane, int q_len, int L, bool causal,
+                                                int row0 = 0) {
     const int row = row0 + (lane & 15);
     if (row >= q_len * p.g) return 0;
-    return p.causal ? min(L, L - q_len + row / p.g + 1) : L;
+    return causal ? min(L, L - q_len + row / p.g + 1) : L;
 }
 
 // One wave's share of a decode work item: keys [k_first, k_end) of request r,
@@ -294,7 +295,7 @@ __device__ __forceinline__ void decode_range(const FwdParams& p, uint16_t* stage
     constexpr int NL = DT::NL;
     u32x4 qf[DT::KS];
     load_decode_q<HD>(p, lane, q0, q_len * p.g, kh, qf);
-    const int limit = min(decode_row_limit(p, lane, q_len, L), k_end);
+    const int limit = min(decode_row_limit(p, lane, q_len, L, p.causal), k_end);
     const int lo = VAR ? decode_row_lo(p, lane, q_len, L) : 0;
     const float al2 = VAR ? decode_row_alibi(p, lane, kh) : 0.f;
     const int qpos = decode_row_pos(p, lane, q_len, L);
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int pos = min(c.key0() + DT::key_of(lane, i), c.L - 1);
-            if constexpr (PAGED) pg[i] = p.bt[(int64_t)c.r * p.bt_stride + page_index(pos, p.bs, p.bs_shift)];
+            if constexpr (PAGED) pg[i] = req_bt(p, c.r)[page_index(pos, p.bs, p.bs_shift)];
             else pg[i] = c.q0 + pos;
         }
     };
@@ -664,7 +665,7 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         load_decode_q<HD>(p, lane, c0.q0, c0.q_len * p.g, c0.kh, qf[rb], 16 * rb);
-        limit[rb] = decode_row_limit(p, lane, c0.q_len, c0.L, 16 * rb);
+        limit[rb] = decode_row_limit(p, lane, c0.q_len, c0.L, req_causal(p, c0.r), 16 * rb);
         lo[rb] = VAR ? decode_row_lo(p, lane, c0.q_len, c0.L, 16 * rb) : 0;
         al2[rb] = VAR ? decode_row_alibi(p, lane, c0.kh, 16 * rb) : 0.f;
         qpos[rb] = decode_row_pos(p, lane, c0.q_len, c0.L, 16 * rb);
@@ -691,7 +692,8 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
     bool w_whole = false;
     DecodeCursor wc = c0;
     auto close = [&](const DecodeCursor& c) {
-        w_whole = seg_t0 == 0 && c.t == c.n - 1;
+        // (a cascade's partial states all go to the merge: none is final)
+        w_whole = seg_t0 == 0 && c.t == c.n - 1 && p.casc_len == 0;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             float l = l_run[rb], lc = lc_run[rb];
@@ -805,7 +807,7 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
                     load_decode_q<HD>(p, lane, c0.q0, c0.q_len * p.g, c0.kh, qf[rb], 16 * rb);
                     sk[rb] = has_sinks ? sink_l2(p, head_of(c0.kh, rb)) : -INFINITY;
                 }
-                limit[rb] = decode_row_limit(p, lane, c0.q_len, c0.L, 16 * rb);
+                limit[rb] = decode_row_limit(p, lane, c0.q_len, c0.L, req_causal(p, c0.r), 16 * rb);
                 if constexpr (VAR) {
                     lo[rb] = decode_row_lo(p, lane, c0.q_len, c0.L, 16 * rb);
                     al2[rb] = decode_row_alibi(p, lane, c0.kh, 16 * rb);
@@ -1581,6 +1583,100 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
     if (p.lse && hl == 0) p.lse[(int64_t)h * p.T + tok] = lse;
 }
 
+// Merge for a cascade run as one balanced decode (casc_len > 0): request 0
+// of the decode list is every token against the shared prefix, request r >= 1
+// is request r - 1 against its own keys, and every segment left a partial
+// state. One half-wave per row of a suffix item (request r >= 1, kv head kh):
+// it folds the partials of that item and those of the prefix item (request 0,
+// the same kv head) at the row of the same token and head, by log-sum-exp,
+// and adds a sink logit to the normaliser once.
+template <int CH>
+__global__ __launch_bounds__(256) void combine_cascade_kernel(FwdParams p) {
+    const int lane = threadIdx.x & 63;
+    const int hl = lane & 31;
+    const int wgs = p.dec_rows >> 3;  // workgroups per item
+    const int64_t sitem = blockIdx.x / wgs;
+    const int r = 1 + (int)(sitem / p.Hkv);
+    const int kh = (int)(sitem % p.Hkv);
+    const int row16 = (int)((blockIdx.x % wgs) * 8 + (threadIdx.x >> 5));
+    const int q0 = req_q0(p, r);
+    const int q_len = req_qend(p, r) - q0;
+    if (row16 >= q_len * p.g) return;  // whole half-waves leave together
+    const int64_t tok = q0 + row16 / p.g;
+    const int h = kh * p.g + row16 % p.g;
+    const int64_t N = (int64_t)p.Hkv * p.sk_prefix[p.B];
+    const int64_t W = p.sk_waves;
+    auto owns_tiles = [&](int64_t w) { return (w + 1) * N / W > w * N / W; };
+    const int nch = p.hd / 4;
+    const bool c0 = hl < nch, c1 = hl + 32 < nch;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 o0 = zero, o1 = zero;
+    float wsum = 0.f, M = -INFINITY;
+    // the prefix item's row of this token and head, then this row of the suffix item
+#pragma unroll 1
+    for (int part = 0; part < 2; ++part) {
+        const int rr = part == 0 ? 0 : r;
+        const int row = part == 0 ? (int)(tok * p.g + row16 % p.g) : row16;
+        const int ql = req_qend(p, rr) - req_q0(p, rr);
+        const int n = decode_tiles_of(p, ql, req_L(p, rr, ql));
+        if (n == 0) continue;
+        const int64_t item = (int64_t)rr * p.Hkv + kh;
+        const int64_t g0 = (int64_t)p.Hkv * p.sk_prefix[rr] + (int64_t)kh * n;
+        const int64_t wf = wave_of_tile(g0, N, W), wl = wave_of_tile(g0 + n - 1, N, W);
+        const int64_t slot0 = wf + item;
+        const int np = (int)(wl - wf + 1);
+        for (int j0 = 0; j0 < np; j0 += CH) {
+            const int jl = j0 + hl;
+            const float lsl = hl < CH && jl < np && owns_tiles(wf + jl)
+                                  ? p.part_lse[(slot0 + jl) * p.dec_rows + row] : -INFINITY;
+            float ls[CH];
+            f32x4 v0[CH], v1[CH];
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+                ls[u] = __shfl(lsl, (lane & 32) + u);
+                v0[u] = zero;
+                v1[u] = zero;
+                if (j0 + u < np) {
+                    const float* src = p.part_o + ((slot0 + j0 + u) * p.dec_rows + row) * p.hd;
+                    if (c0) v0[u] = *(const f32x4*)(src + 4 * hl);
+                    if (c1) v1[u] = *(const f32x4*)(src + 4 * (hl + 32));
+                }
+            }
+            float cm = M;
+#pragma unroll
+            for (int u = 0; u < CH; ++u) cm = fmaxf(cm, ls[u]);
+            if (cm == -INFINITY) continue;
+            const float a = fast_exp2((M - cm) * kLog2e);
+            o0 *= a;
+            o1 *= a;
+            wsum *= a;
+            M = cm;
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+                const float wj = fast_exp2((ls[u] - M) * kLog2e);
+                wsum += wj;
+                if (wj != 0.f) {  // an absent partial's slot holds stale bytes
+                    o0 += wj * v0[u];
+                    o1 += wj * v1[u];
+                }
+            }
+        }
+    }
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float inv, lse;
+    finalize_row(Mu * kLog2e, wsum, sink_l2(p, h), 1.f, inv, lse);
+    uint16_t* dst = (uint16_t*)p.out + (tok * p.H + h) * p.hd;
+    if (c0) {
+        o0 *= inv;
+        *(u32x2*)(dst + 4 * hl) = u32x2{pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3])};
+    }
+    if (c1) {
+        o1 *= inv;
+        *(u32x2*)(dst + 4 * (hl + 32)) = u32x2{pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
+    }
+    if (p.lse && hl == 0) p.lse[(int64_t)h * p.T + tok] = lse;
+}
+
 template <bool F32>
 __device__ __forceinline__ f32x4 load4(const void* base, int64_t e) {
     if constexpr (F32) {
@@ -1692,6 +1788,14 @@ hipError_t launch_combine_balanced(const FwdParams& p, hipStream_t s) {
     // 16 partials pay off from about 16 partials per item
     if (p.sk_waves >= 16 * items) hipLaunchKernelGGL(combine_balanced_kernel<16>, grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL(combine_balanced_kernel<4>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_cascade(const FwdParams& p, hipStream_t s) {
+    const int64_t items = (int64_t)(p.B - 1) * p.Hkv;  // suffix items; dec_rows / 8 workgroups each
+    const dim3 grid((unsigned)(items * (p.dec_rows / 8)));
+    if (p.sk_waves >= 16 * items) hipLaunchKernelGGL(combine_cascade_kernel<16>, grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(combine_cascade_kernel<4>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

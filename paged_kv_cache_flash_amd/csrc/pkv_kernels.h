@@ -45,17 +45,35 @@ struct FwdParams {
     int32_t seq_off;          // keys before this index belong to another pass: request r's
                               // KV length is max(0, seq_lens[r] - seq_off), and the block
                               // table passed in starts at that key's page
+    int32_t casc_len;         // > 0: both cascade passes in one balanced decode launch. Request 0
+                              // is every token against the first casc_len keys of block-table
+                              // row 0, with no causal mask; request r >= 1 is request r - 1
+                              // against its own keys from casc_len on. B counts both.
 };
 
 // Request metadata as every kernel reads it (cascade passes included).
-__device__ __forceinline__ int req_q0(const FwdParams& p, int r) { return p.single_len > 0 ? 0 : p.qsl[r]; }
+__device__ __forceinline__ int req_q0(const FwdParams& p, int r) {
+    if (p.casc_len > 0) return r == 0 ? 0 : p.qsl[r - 1];
+    return p.single_len > 0 ? 0 : p.qsl[r];
+}
 __device__ __forceinline__ int req_qend(const FwdParams& p, int r) {
+    if (p.casc_len > 0) return r == 0 ? (int)p.T : p.qsl[r];
     return p.single_len > 0 ? (int)p.T : p.qsl[r + 1];
 }
 // KV length of request r with q_len query tokens (q_len itself in the flat layout).
 __device__ __forceinline__ int req_L(const FwdParams& p, int r, int q_len) {
+    if (p.casc_len > 0) return r == 0 ? p.casc_len : max(0, p.seq_lens[r - 1] - p.casc_len);
     if (p.single_len > 0) return p.single_len;
     return p.seq_lens ? max(0, p.seq_lens[r] - p.seq_off) : q_len;
+}
+// Block-table entries of request r's keys, from its first key on.
+__device__ __forceinline__ const int32_t* req_bt(const FwdParams& p, int r) {
+    if (p.casc_len > 0) return r == 0 ? p.bt : p.bt + (int64_t)(r - 1) * p.bt_stride + p.casc_len / p.bs;
+    return p.bt + (int64_t)r * p.bt_stride;
+}
+// Whether request r's keys take the causal mask.
+__device__ __forceinline__ bool req_causal(const FwdParams& p, int r) {
+    return p.causal && !(p.casc_len > 0 && r == 0);
 }
 
 enum class KvType { BF16, FP8, F32 };
@@ -70,6 +88,7 @@ hipError_t scratch_for_current_device(void** ptr);
 hipError_t launch_decode(const FwdParams& p, KvType kv, hipStream_t s);
 hipError_t launch_decode_balanced(const FwdParams& p, KvType kv, hipStream_t s);
 hipError_t launch_combine_balanced(const FwdParams& p, hipStream_t s);
+hipError_t launch_combine_cascade(const FwdParams& p, hipStream_t s);
 hipError_t launch_prefill(const FwdParams& p, KvType kv, bool q8, hipStream_t s);
 hipError_t launch_generic(const FwdParams& p, KvType kv, bool q_f32, hipStream_t s);
 hipError_t launch_combine(const FwdParams& p, bool out_f32, hipStream_t s);
