@@ -213,7 +213,10 @@ def cascade_sweep():
         return torch.from_numpy(a).to(dev)
     for B, L, P in ((4, 131072, 32768), (4, 131072, 49152), (4, 131072, 65536), (4, 131072, 98304),
                     (8, 131072, 98304), (2, 262144, 196608), (8, 65536, 49152), (4, 131072, 8192),
-                    (8, 16384, 8192), (16, 8192, 4096), (16, 4096, 512), (32, 8192, 2048), (64, 2048, 1024)):
+                    (8, 16384, 8192), (16, 8192, 4096), (16, 4096, 512), (32, 8192, 2048), (64, 2048, 1024),
+                    (2, 131072, 32768), (2, 131072, 65536), (3, 131072, 65536), (4, 65536, 32768),
+                    (4, 32768, 16384), (4, 16384, 8192), (2, 32768, 16384), (8, 32768, 16384), (16, 16384, 8192),
+                    (4, 131072, 16384), (3, 65536, 16384)):
         prob = workloads.long_decode(B=B, L=L, shared_prefix=P)
         reps = []
         for _ in range(3):
@@ -249,7 +252,7 @@ def cascade_sweep():
             g.replay()
             torch.cuda.synchronize()
             us[name] = (time.perf_counter() - t) / 30 * 1e6
-        use, tp, tc = pkv.use_cascade_attention(P, prob.seq_lens, prob.Hkv, prob.hd)
+        use, tp, tc = pkv.use_cascade_attention(P, prob.seq_lens, prob.T, prob.H, prob.Hkv, prob.hd)
         print(json.dumps({"batch": B, "seq_len": L, "shared_prefix": P, "plain_us": round(us["plain"], 1),
                           "cascade_us": round(us["cascade"], 1), "model_plain_us": round(tp, 1),
                           "model_cascade_us": round(tc, 1), "chosen": "cascade" if use else "plain",

@@ -250,6 +250,11 @@ pkv_status pkv_merge_attn_states(void* out, float* out_lse, const void* prefix_o
  *   3. pkv_merge_attn_states of the two states into a->out (and a->lse).
  * The result equals pkv_varlen_fwd over the whole batch, with the shared
  * pages read once instead of once per request.
+ * When the whole batch fits one item of the balanced decode (bf16 q,
+ * num_tokens x the group at most 16 query rows, or 32 with head size up to
+ * 128), the three steps run as one decode launch and one merge launch: the
+ * prefix pass joins the decode's tile list as a further request, and the
+ * merge folds its partial states into each row with the suffix's.
  * `a` describes the whole batch exactly as for pkv_varlen_fwd (block_table
  * required); both passes and the merge run inside the library on `stream`.
  * Preconditions (device data, not checked): every request's first
@@ -271,24 +276,31 @@ size_t pkv_cascade_workspace_size(const pkv_varlen_args* a, int32_t common_prefi
 pkv_status pkv_cascade_fwd(const pkv_varlen_args* a, int32_t common_prefix_len, void* stream);
 
 /* Whether to run a batch whose requests share their first common_prefix_len
- * KV tokens (the same pages) as a cascade: a prefix pass, a suffix pass and
- * pkv_merge_attn_states. The deep-dive page's decision (cascade attention
+ * KV tokens (the same pages) as a cascade (pkv_cascade_fwd) rather than
+ * plainly (pkv_varlen_fwd). The deep-dive page's decision (cascade attention
  * section) first rules it out for a prefix under 256 tokens and for sliding
  * windows; its remaining test, a performance model, is not printed, and its
  * request-count rule (fewer than 8 requests: no) is that model's stand-in for
  * its own kernels. Here a model of this library's decode kernels takes both
- * places, fitted to MI355X measurements: both forms read the unique keys
- * (the prefix once, every suffix) at 5.2 TB/s; the plain form also re-reads
- * the shared pages once per further request, and the 256 MB last-level cache
- * serves most of those: the share that reaches HBM grows from 0 at 0.55 GB
- * of re-read bytes to 35% at 1.2 GB and beyond; the cascade adds 50 us for
- * its extra launches (prefix-pass merge, final merge). Bytes per key:
+ * places, fitted to MI355X measurements of 24 shared-prefix decode batches
+ * (1 to 64 requests, 2K to 256K keys): the plain form reads the unique keys
+ * (the prefix once, every suffix) at 5.6 TB/s plus 17 us, and of its
+ * re-reads of the shared pages (once per further request) a share reaches
+ * HBM that grows with the prefix's part of the mean KV length f: 0 up to
+ * f = 0.2, then 2.4 (f - 0.2), at most 0.6 (the last-level cache serves the
+ * rest, as far as the requests' reads of a page fall close in time); the
+ * cascade reads the unique keys only, at 5.4 TB/s plus 28 us as one launch
+ * (see pkv_cascade_fwd: num_tokens and num_heads decide whether it applies,
+ * for a bf16 q) and at 5.5 TB/s plus 40 us as three. Bytes per key:
  * num_kv_heads * head_size * 2 * element bytes.
- * host_seq_lens: num_seqs KV lengths in host memory. Writes 1 (cascade) or 0
- * to *use_cascade and, when not NULL, the two predicted times in us.        */
+ * host_seq_lens: num_seqs KV lengths in host memory; num_tokens: query tokens
+ * of the batch. Writes 1 (cascade) or 0 to *use_cascade and, when not NULL,
+ * the two predicted times in us. INVALID_ARG for negative sizes or lengths,
+ * num_heads not a positive multiple of num_kv_heads, or NULL use_cascade.    */
 pkv_status pkv_cascade_choose(int32_t common_prefix_len, int32_t num_seqs, const int32_t* host_seq_lens,
-                              int32_t num_kv_heads, int32_t head_size, pkv_dtype kv_dtype, int32_t sliding_window,
-                              int32_t* use_cascade, double* t_plain_us, double* t_cascade_us);
+                              int64_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                              pkv_dtype kv_dtype, int32_t sliding_window, int32_t* use_cascade, double* t_plain_us,
+                              double* t_cascade_us);
 
 /* ------------------------------------------------------------------ utilities */
 

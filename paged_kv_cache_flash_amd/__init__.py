@@ -108,7 +108,7 @@ def lib() -> ctypes.CDLL:
     L.pkv_cascade_fwd.restype = i32
     L.pkv_cascade_fwd.argtypes = [ctypes.POINTER(pkv_varlen_args), i32, vp]
     L.pkv_cascade_choose.restype = i32
-    L.pkv_cascade_choose.argtypes = [i32, i32, vp, i32, i32, i32, i32, vp, vp, vp]
+    L.pkv_cascade_choose.argtypes = [i32, i32, vp, i64, i32, i32, i32, i32, i32, vp, vp, vp]
     L.pkv_last_error.restype = ctypes.c_char_p
     L.pkv_last_error.argtypes = []
     L.pkv_version.restype = i32
@@ -293,17 +293,19 @@ def pkv_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suff
     return out
 
 
-def use_cascade_attention(common_prefix_len, seq_lens, num_kv_heads, head_size, kv_dtype=PKV_BF16,
-                          sliding_window=0):
+def use_cascade_attention(common_prefix_len, seq_lens, num_tokens, num_heads, num_kv_heads, head_size,
+                          kv_dtype=PKV_BF16, sliding_window=0):
     """Whether the cascade form is predicted to be faster (pkv_cascade_choose); seq_lens is a host
-    sequence of KV lengths. Returns (use, predicted plain us, predicted cascade us)."""
+    sequence of KV lengths, num_tokens the batch's query tokens. Returns (use, predicted plain us,
+    predicted cascade us)."""
     import numpy as np
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
     use = ctypes.c_int32(0)
     tp, tc = ctypes.c_double(0.0), ctypes.c_double(0.0)
     _check(lib().pkv_cascade_choose(int(common_prefix_len), len(sl), sl.ctypes.data_as(ctypes.c_void_p),
-                                    int(num_kv_heads), int(head_size), int(kv_dtype), int(sliding_window),
-                                    ctypes.byref(use), ctypes.byref(tp), ctypes.byref(tc)))
+                                    int(num_tokens), int(num_heads), int(num_kv_heads), int(head_size),
+                                    int(kv_dtype), int(sliding_window), ctypes.byref(use), ctypes.byref(tp),
+                                    ctypes.byref(tc)))
     return bool(use.value), tp.value, tc.value
 
 

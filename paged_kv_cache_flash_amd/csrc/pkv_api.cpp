@@ -373,6 +373,17 @@ struct Cascade {
     PassOpts one_o;
 };
 
+// Whether a cascade runs as one balanced decode launch: `one` is the batch
+// with the prefix pass as a further request of every token (num_seqs + 1,
+// max_seqlen_q = num_tokens).
+bool one_launch_cascade(const pkv_varlen_args& one) {
+    if (one.num_splits != 0) return false;
+    const std::string err = g_err;  // (a failed check here is no error of the caller's)
+    const bool valid = validate_sizes(&one) == PKV_OK;
+    g_err = err;
+    return valid && make_plan(&one).kind == Kind::DecodeBalanced;
+}
+
 pkv_status cascade_plan(const pkv_varlen_args* a, int32_t P, Cascade& c) {
     if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
     if (!a->block_table) return fail(PKV_ERR_INVALID_ARG, "a cascade needs a paged cache (block_table)");
@@ -413,19 +424,13 @@ pkv_status cascade_plan(const pkv_varlen_args* a, int32_t P, Cascade& c) {
     c.total = 2 * (c.o_bytes + c.l_bytes) + c.pass_ws;
     // The one-launch form, when the batch is decode-shaped: all of its query
     // rows (every token x the group) fit one item of the balanced decode.
-    c.fused = false;
     c.one = *a;
     c.one.num_seqs = a->num_seqs + 1;
     c.one.max_seqlen_q = T;
     c.one_o = PassOpts{};
     c.one_o.casc_len = P;
-    if (a->num_splits == 0 && validate_sizes(&c.one) == PKV_OK) {
-        const Plan pl = make_plan(&c.one);
-        if (pl.kind == Kind::DecodeBalanced) {
-            c.fused = true;
-            c.total = pl.workspace;
-        }
-    }
+    c.fused = one_launch_cascade(c.one);
+    if (c.fused) c.total = make_plan(&c.one).workspace;
     return ok();
 }
 
@@ -549,19 +554,23 @@ pkv_status pkv_merge_attn_states(void* out, float* out_lse, const void* prefix_o
 }
 
 pkv_status pkv_cascade_choose(int32_t common_prefix_len, int32_t num_seqs, const int32_t* host_seq_lens,
-                              int32_t num_kv_heads, int32_t head_size, pkv_dtype kv_dtype, int32_t sliding_window,
-                              int32_t* use_cascade, double* t_plain_us, double* t_cascade_us) {
-    // decode read rate, fixed cost of the cascade's extra launches, and the
-    // share of the plain form's prefix re-reads that reach HBM (the 256 MB
-    // last-level cache serves the rest): 0 up to 0.55 GB of re-read bytes,
-    // rising by 1 per 1.8 GB to at most 35%; all fitted to measurements on
-    // MI355X (13 shared-prefix decode batches)
-    constexpr double kBytesPerUs = 5.2e6;
-    constexpr double kCascadeFixedUs = 50.0;
-    constexpr double kRereadFree = 0.55e9, kRereadSlope = 1.8e9, kRereadMissMax = 0.35;
+                              int64_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                              pkv_dtype kv_dtype, int32_t sliding_window, int32_t* use_cascade, double* t_plain_us,
+                              double* t_cascade_us) {
+    // Read rates (bytes per us) and fixed costs of the plain decode and the
+    // two cascade forms, and the share of the plain form's prefix re-reads
+    // that reach HBM as a ramp in the prefix's part of the mean KV length;
+    // all fitted to measurements on MI355X (24 shared-prefix decode batches,
+    // the cascade forms by least squares, the ramp by the time a wrong choice
+    // costs)
+    constexpr double kPlainRate = 5.6e6, kPlainFixedUs = 17.0;
+    constexpr double kOneRate = 5.4e6, kOneFixedUs = 28.0;
+    constexpr double kThreeRate = 5.5e6, kThreeFixedUs = 40.0;
+    constexpr double kMissFrom = 0.2, kMissSlope = 2.4, kMissMax = 0.6;
     constexpr int32_t kMinPrefix = 256;
-    if (!use_cascade || num_seqs < 0 || (num_seqs > 0 && !host_seq_lens) || num_kv_heads <= 0 || head_size <= 0 ||
-        common_prefix_len < 0 || sliding_window < 0)
+    if (!use_cascade || num_seqs < 0 || (num_seqs > 0 && !host_seq_lens) || num_tokens < 0 || num_heads <= 0 ||
+        num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_size <= 0 || common_prefix_len < 0 ||
+        sliding_window < 0)
         return fail(PKV_ERR_INVALID_ARG, "invalid cascade query");
     if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3FN && kv_dtype != PKV_F32)
         return fail(PKV_ERR_UNSUPPORTED, "unknown kv_dtype %d", (int)kv_dtype);
@@ -575,9 +584,32 @@ pkv_status pkv_cascade_choose(int32_t common_prefix_len, int32_t num_seqs, const
     }
     const int64_t rereads = prefix_fits ? (int64_t)(num_seqs - 1) * common_prefix_len : 0;
     const int64_t unique = keys - rereads;
-    const double miss = std::min(kRereadMissMax, std::max(0.0, (rereads * per_key - kRereadFree) / kRereadSlope));
-    const double tp = (unique + miss * rereads) * per_key / kBytesPerUs;
-    const double tc = unique * per_key / kBytesPerUs + kCascadeFixedUs;
+    const double f = keys > 0 ? (double)common_prefix_len * num_seqs / (double)keys : 0.0;
+    const double miss = std::min(kMissMax, std::max(0.0, kMissSlope * (f - kMissFrom)));
+    const double tp = kPlainFixedUs + (unique + miss * rereads) * per_key / kPlainRate;
+    // the batch as pkv_cascade_fwd would see it (a bf16 q; the table itself
+    // is never read here)
+    pkv_varlen_args one{};
+    int32_t max_len = 0;
+    for (int32_t r = 0; r < num_seqs; ++r) max_len = std::max(max_len, host_seq_lens[r]);
+    one.num_tokens = num_tokens;
+    one.num_seqs = num_seqs + 1;
+    one.num_heads = num_heads;
+    one.num_kv_heads = num_kv_heads;
+    one.head_size = head_size;
+    one.q_dtype = kv_dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
+    one.kv_dtype = kv_dtype;
+    one.softmax_scale = 1.f;
+    one.causal = 1;
+    one.max_seqlen_q = (int32_t)std::min<int64_t>(std::max<int64_t>(num_tokens, 1), INT32_MAX);
+    one.max_seqlen_k = std::max(max_len, one.max_seqlen_q);
+    one.block_table = &max_len;  // (any non-NULL address: a paged batch)
+    one.block_size = 16;
+    one.num_blocks = 1;
+    one.block_table_stride = cdiv(one.max_seqlen_k, one.block_size);
+    const bool one_launch = num_tokens > 0 && one_launch_cascade(one);
+    const double tc = one_launch ? kOneFixedUs + unique * per_key / kOneRate
+                                 : kThreeFixedUs + unique * per_key / kThreeRate;
     if (t_plain_us) *t_plain_us = tp;
     if (t_cascade_us) *t_cascade_us = tc;
     *use_cascade = common_prefix_len >= kMinPrefix && sliding_window == 0 && prefix_fits && tc < tp ? 1 : 0;

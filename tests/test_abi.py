@@ -267,37 +267,81 @@ def test_product_path_never_imports_the_oracle():
                 assert "import oracle" not in text and "liboracle" not in text and "pkv_oracle" not in text, f
 
 
-def test_cascade_choice():
+# Decode batches whose requests share a prefix (one new token per request,
+# 64/8 heads, head 128, bf16, page 256), timed on MI355X by
+# `python bench.py --cascade-sweep`: (requests, KV length, shared prefix,
+# plain us, cascade us), each the mean of one HIP graph of 30 forwards
+# (the run in profiles/cascade_choice_sweep.md).
+CASCADE_SWEEP = [
+    (4, 131072, 32768, 326.5, 342.8),
+    (4, 131072, 49152, 317.5, 318.8),
+    (4, 131072, 65536, 318.9, 283.6),
+    (4, 131072, 98304, 300.3, 202.6),
+    (8, 131072, 98304, 546.8, 303.9),
+    (2, 262144, 196608, 324.2, 272.4),
+    (8, 65536, 49152, 283.4, 187.7),
+    (4, 131072, 8192, 382.2, 406.1),
+    (8, 16384, 8192, 94.1, 97.3),
+    (16, 8192, 4096, 91.2, 90.0),
+    (16, 4096, 512, 61.4, 78.6),
+    (32, 8192, 2048, 180.9, 182.3),
+    (64, 2048, 1024, 94.2, 87.9),
+    (2, 131072, 32768, 190.8, 199.4),
+    (2, 131072, 65536, 180.0, 175.1),
+    (3, 131072, 65536, 309.6, 228.8),
+    (4, 65536, 32768, 172.6, 153.9),
+    (4, 32768, 16384, 100.3, 89.0),
+    (4, 16384, 8192, 60.3, 56.5),
+    (2, 32768, 16384, 64.1, 66.2),
+    (8, 32768, 16384, 171.6, 148.9),
+    (16, 16384, 8192, 167.0, 141.8),
+    (4, 131072, 16384, 362.9, 389.5),
+    (3, 65536, 16384, 155.1, 152.4)
+]
+
+
+def test_cascade_choice_rules():
     # the pages' rules: a prefix under 256 tokens or a sliding window: no
-    use, tp, tc = pkv.use_cascade_attention(255, [100000] * 16, 8, 128)
+    use, tp, tc = pkv.use_cascade_attention(255, [100000] * 16, 16, 128, 8, 128)
     assert not use
-    use, _, _ = pkv.use_cascade_attention(32768, [131072] * 4, 8, 128, sliding_window=4096)
+    use, _, _ = pkv.use_cascade_attention(98304, [131072] * 4, 4, 64, 8, 128, sliding_window=4096)
     assert not use
-    # four requests of 131072 keys sharing 32768: the plain form re-reads
-    # 3 x 134 MB of prefix K/V, which the last-level cache serves, so the
-    # cascade only adds its fixed 50 us
-    unique = 4 * 131072 - 3 * 32768
-    use, tp, tc = pkv.use_cascade_attention(32768, [131072] * 4, 8, 128)
-    assert not use
-    assert abs(tp - unique * 4096 / 5.2e6) < 1e-6
-    assert abs(tc - unique * 4096 / 5.2e6 - 50.0) < 1e-6
-    # sharing 98304 (3 x 403 MB re-read): 35% of the re-reads reach HBM, more
-    # than the cascade's fixed cost
-    unique = 4 * 131072 - 3 * 98304
-    use, tp, tc = pkv.use_cascade_attention(98304, [131072] * 4, 8, 128)
-    assert use
-    assert abs(tp - (unique + 0.35 * 3 * 98304) * 4096 / 5.2e6) < 1e-6
-    # sharing 65536 (0.81 GB re-read): a 14% share, not enough
-    use, tp, tc = pkv.use_cascade_attention(65536, [131072] * 4, 8, 128)
-    assert not use
-    miss = (3 * 65536 * 4096 - 0.55e9) / 1.8e9
-    assert abs(tp - (4 * 131072 - 3 * 65536 + miss * 3 * 65536) * 4096 / 5.2e6) < 1e-6
-    # a short shared prefix saves too little
-    use, tp, tc = pkv.use_cascade_attention(512, [4096] * 8, 8, 128)
-    assert not use and tc > tp
     # every request must keep at least one token of its own
-    use, _, _ = pkv.use_cascade_attention(4096, [4096, 8192], 8, 128)
+    use, _, _ = pkv.use_cascade_attention(4096, [4096, 8192], 2, 64, 8, 128)
     assert not use
     # invalid queries
-    with pytest.raises(RuntimeError):
-        pkv.use_cascade_attention(-1, [10], 8, 128)
+    for bad in ((-1, [10], 1, 8, 8, 128), (256, [1000], -1, 8, 8, 128), (256, [1000], 1, 12, 8, 128),
+                (256, [-5], 1, 8, 8, 128)):
+        with pytest.raises(RuntimeError):
+            pkv.use_cascade_attention(*bad)
+
+
+def test_cascade_choice_against_measurements():
+    """The choice against the measured sweep: where one form was faster by
+    more than 10%, that is the form chosen; over the whole sweep the time lost
+    to choosing the slower form stays under 1% of the best total; and each
+    predicted time is within 20% of the measured one."""
+    lost = best = 0.0
+    for B, L, P, plain_us, casc_us in CASCADE_SWEEP:
+        use, tp, tc = pkv.use_cascade_attention(P, [L] * B, B, 64, 8, 128)
+        what = f"B={B} L={L} P={P}: measured {plain_us}/{casc_us}, predicted {tp:.1f}/{tc:.1f}"
+        if casc_us < 0.9 * plain_us:
+            assert use, what
+        if plain_us < 0.9 * casc_us:
+            assert not use, what
+        best += min(plain_us, casc_us)
+        lost += (casc_us if use else plain_us) - min(plain_us, casc_us)
+        assert abs(tp - plain_us) < 0.2 * plain_us and abs(tc - casc_us) < 0.2 * casc_us, what
+    assert lost < 0.01 * best, (lost, best)
+
+
+def test_cascade_choice_form():
+    # four requests x 8 heads of a group = 32 query rows at head size 128: one
+    # launch; at head size 256 (16 rows at most) or with eight requests: three
+    _, _, one = pkv.use_cascade_attention(65536, [131072] * 4, 4, 64, 8, 128)
+    unique = (65536 + 4 * 65536) * 8 * 128 * 2 * 2
+    assert abs(one - (28.0 + unique / 5.4e6)) < 1e-6
+    _, _, three = pkv.use_cascade_attention(65536, [131072] * 4, 4, 64, 8, 256)
+    assert abs(three - (40.0 + 2 * unique / 5.5e6)) < 1e-6
+    _, _, three = pkv.use_cascade_attention(65536, [131072] * 8, 8, 64, 8, 128)
+    assert abs(three - (40.0 + (65536 + 8 * 65536) * 4096 / 5.5e6)) < 1e-6
