@@ -240,6 +240,119 @@ struct DecodeTile {
             oacc[mb] = mfma16x16x32(vf, pf, oacc[mb]);
         }
     }
+
+    // The first N of an item's RB blocks of 16 query rows over one tile, as
+    // compute() does for one block, except that every K and V fragment read
+    // from LDS feeds the MFMAs of all N blocks, and that the running output is
+    // rescaled lazily: only when some row's tile maximum exceeds its running
+    // maximum by more than kLazyRescale (log2 domain; a wave-uniform
+    // decision), so that the probabilities stay below 2^kLazyRescale and the
+    // accumulators are otherwise touched by the MFMAs alone.
+    template <bool VAR, bool DL, int N, int RB>
+    static __device__ __forceinline__ void compute_rows(const uint16_t* stage, int lane, int t0, const int (&lo)[RB],
+                                                        const int (&limit)[RB], float sl2, float cap_l2,
+                                                        float cap_inv2, const float (&al2)[RB], const int (&qpos)[RB],
+                                                        const u32x4 (&qf)[RB][KS], float (&m_run)[RB],
+                                                        float (&l_run)[RB], float (&lc_run)[RB],
+                                                        f32x4 (&oacc)[RB][MB]) {
+        static_assert(N >= 1 && N <= RB, "");
+        const uint16_t* const kl = stage;
+        const uint16_t* const vl = stage + K_ELEMS;
+        const uint8_t* const st = (const uint8_t*)stage;
+        const int row = lane & 15;
+        const int G = lane >> 4;
+        f32x4 sacc[N][2];
+        const uint16_t* kp = kl + row * KP + G * 8;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) sacc[n][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int swk = dsw(b * 16 + row);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 kf;
+                if constexpr (DL && FP8)
+                    kf = fp8x8_to_bf16x8(*(const u32x2*)(st + (b * 16 + row) * ROW_BYTES +
+                                                         (((2 * ks + (G >> 1)) ^ swk) << 4) + (G & 1) * 8));
+                else if constexpr (DL)
+                    kf = *(const u32x4*)(st + (b * 16 + row) * ROW_BYTES + (((G + 4 * ks) ^ swk) << 4));
+                else
+                    kf = *(const u32x4*)(kp + b * 16 * KP + ks * 32);
+#pragma unroll
+                for (int n = 0; n < N; ++n) sacc[n][b] = mfma16x16x32(kf, qf[n][ks], sacc[n][b]);
+            }
+        }
+        u32x4 pf[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            float sv[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = t0 + b * 16 + G * 4 + i;
+                    float x = sacc[n][b][i] * sl2;
+                    if constexpr (VAR) {
+                        if (cap_l2 > 0.f) x = softcap_l2(x, cap_l2, cap_inv2);
+                        if (al2[n] != 0.f) x -= al2[n] * fabsf((float)(qpos[n] - key));
+                        x = key < limit[n] && key >= lo[n] ? x : -INFINITY;
+                    } else {
+                        x = key < limit[n] ? x : -INFINITY;
+                    }
+                    sv[b * 4 + i] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (__any(mx > m_run[n] + kLazyRescale)) {
+                const float m_new = fmaxf(m_run[n], mx);
+                const float alpha = fast_exp2(m_run[n] - (m_new == -INFINITY ? 0.f : m_new));
+                l_run[n] *= alpha;
+                lc_run[n] *= alpha;
+#pragma unroll
+                for (int i = 0; i < MB; ++i) oacc[n][i] *= alpha;
+                m_run[n] = m_new;
+            }
+            const float m_use = m_run[n] == -INFINITY ? 0.f : m_run[n];
+            float ps = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                sv[j] = fast_exp2(sv[j] - m_use);
+                ps += sv[j];
+            }
+            l_run[n] += ps;
+            pf[n] = u32x4{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]), pack_bf16x2(sv[4], sv[5]),
+                          pack_bf16x2(sv[6], sv[7])};
+            lc_run[n] = add_bf16_pair(pf[n].w, add_bf16_pair(pf[n].z, add_bf16_pair(pf[n].y,
+                                                                                 add_bf16_pair(pf[n].x, lc_run[n]))));
+        }
+        const uint16_t* vt = vl + (G * 4 + ((lane & 15) >> 2)) * VP + (lane & 3) * 4;
+        const int rv = FP8 ? 16 * (((lane & 15) >> 1) >> 2) + 4 * G + (((lane & 15) >> 1) & 3)
+                           : G * 4 + ((lane & 15) >> 2);
+        const int swv = dsw(rv);
+        const uint8_t* const vst = st + DMA_TILE + rv * ROW_BYTES + (lane & 1) * 8;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            u32x4 vf;
+            if constexpr (DL && FP8) {
+                vf = fp8x8_to_bf16x8(lds_read_tr8(vst + ((mb ^ swv) << 4)));
+            } else {
+                u32x2 lo2, hi2;
+                if constexpr (DL) {
+                    const int pos = ((2 * mb + ((lane & 3) >> 1)) ^ swv) << 4;
+                    lo2 = lds_read_tr16(vst + pos);
+                    hi2 = lds_read_tr16(vst + 16 * ROW_BYTES + pos);
+                } else {
+                    lo2 = lds_read_tr16(vt + mb * 16);
+                    hi2 = lds_read_tr16(vt + 16 * VP + mb * 16);
+                }
+                vf = u32x4{lo2.x, lo2.y, hi2.x, hi2.y};
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) oacc[n][mb] = mfma16x16x32(vf, pf[n], oacc[n][mb]);
+        }
+    }
 };
 
 // Query fragment of a decode item: lane l feeds row row0 + l % 16 (token
@@ -504,8 +617,9 @@ struct DecodeCursor {
 
 // RB: blocks of 16 query rows per item (items of up to 16 RB rows); each
 // block is a 16-column MFMA pass over the same K/V tile in LDS. With RB > 1
-// the wave holds RB running states and may use the whole register file (one
-// workgroup per CU).
+// the wave holds RB running states, every K and V fragment it reads feeds
+// the MFMAs of all blocks (DecodeTile::compute_rows), and it may use the
+// whole register file (one workgroup per CU).
 // (bf16 tiles of head size 128 take 128 KB of LDS: one workgroup per CU)
 template <int HD, bool FP8, bool PAGED, bool VAR, int RB>
 __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2 : 1) void decode_balanced_kernel(FwdParams p) {
@@ -513,9 +627,8 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
     constexpr int MB = DT::MB;
     constexpr int NL = DT::NL;
     constexpr int ROWS = 16 * RB;
-    // tiles straight into LDS, two stages per wave (one row block only: with
-    // more, the register file is the constraint and the staged copy is faster)
-    constexpr bool DMA = DT::DMA && RB == 1;
+    // tiles straight into LDS, two stages per wave (head size 128)
+    constexpr bool DMA = DT::DMA;
     static_assert(!DMA || DT::NL * 1024 == DT::DMA_TILE, "one 1 KB copy per load");
     constexpr int SMEM = DMA ? 4 * 2 * DT::DMA_STAGE : 4 * DT::ELEMS * 2;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
@@ -779,13 +892,23 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
             }
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-            if (rb == 0 || 16 * rb < c0.q_len * p.g)  // (a block without rows keeps its empty state)
-                DT::template compute<VAR, DMA>(DMA ? (const uint16_t*)(dstage + par * DT::DMA_STAGE) : stage, lane,
-                                               c0.key0(), lo[rb], limit[rb], sl2, p.softcap_l2, p.softcap_inv2,
-                                               al2[rb], qpos[rb], qf[rb], m_run[rb], l_run[rb], lc_run[rb],
-                                               oacc[rb]);
+        {
+            const uint16_t* const tile = DMA ? (const uint16_t*)(dstage + par * DT::DMA_STAGE) : stage;
+            if constexpr (RB == 1) {
+                DT::template compute<VAR, DMA>(tile, lane, c0.key0(), lo[0], limit[0], sl2, p.softcap_l2,
+                                               p.softcap_inv2, al2[0], qpos[0], qf[0], m_run[0], l_run[0],
+                                               lc_run[0], oacc[0]);
+            } else {
+                // every block, rows or not (a block without rows keeps an
+                // empty state): one instance of the computation per kernel,
+                // since several, chosen by the item's row count, made the
+                // compiler spill; the matrix work of empty blocks hides under
+                // the tile loads
+                DT::template compute_rows<VAR, DMA, RB, RB>(tile, lane, c0.key0(), lo, limit, sl2, p.softcap_l2,
+                                                            p.softcap_inv2, al2, qpos, qf, m_run, l_run, lc_run,
+                                                            oacc);
+            }
+        }
         if (!c1.valid || c1_new) {
             close(c0);
             pending = true;

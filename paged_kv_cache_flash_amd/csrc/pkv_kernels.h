@@ -111,8 +111,10 @@ constexpr int kDecodeWaves = 4;
 constexpr int kBalancedWaves = 1024;
 // Balanced decode items hold up to kDecodeMaxRows query rows (q_len x group)
 // as blocks of 16, for head sizes up to kDecodeMaxRbHead (larger heads: 16).
-// (Four blocks overflow the register file of a wave at head size 128; the
-// prefill kernel then serves such items faster.)
+// (Four blocks fit the register file of a lone wave at head size 128, but
+// their tile computation no longer hides under the tile loads and their
+// partial states cost a tenth of the KV bytes again: the prefill kernel
+// serves such items faster.)
 constexpr int kDecodeMaxRows = 32;
 constexpr int kDecodeMaxRbHead = 128;
 constexpr int kBalancedMaxSeqs = 1024;
