@@ -289,7 +289,7 @@ pkv_status pkv_cascade_fwd(const pkv_varlen_args* a, int32_t common_prefix_len, 
  * HBM that grows with the prefix's part of the mean KV length f: 0 up to
  * f = 0.2, then 2.4 (f - 0.2), at most 0.6 (the last-level cache serves the
  * rest, as far as the requests' reads of a page fall close in time); the
- * cascade reads the unique keys only, at 5.4 TB/s plus 28 us as one launch
+ * cascade reads the unique keys only, at 5.8 TB/s plus 32 us as one launch
  * (see pkv_cascade_fwd: num_tokens and num_heads decide whether it applies,
  * for a bf16 q) and at 5.5 TB/s plus 40 us as three. Bytes per key:
  * num_kv_heads * head_size * 2 * element bytes.

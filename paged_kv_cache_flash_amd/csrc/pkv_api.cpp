@@ -564,7 +564,7 @@ pkv_status pkv_cascade_choose(int32_t common_prefix_len, int32_t num_seqs, const
     // the cascade forms by least squares, the ramp by the time a wrong choice
     // costs)
     constexpr double kPlainRate = 5.6e6, kPlainFixedUs = 17.0;
-    constexpr double kOneRate = 5.4e6, kOneFixedUs = 28.0;
+    constexpr double kOneRate = 5.8e6, kOneFixedUs = 32.0;
     constexpr double kThreeRate = 5.5e6, kThreeFixedUs = 40.0;
     constexpr double kMissFrom = 0.2, kMissSlope = 2.4, kMissMax = 0.6;
     constexpr int32_t kMinPrefix = 256;
