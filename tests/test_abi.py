@@ -138,6 +138,29 @@ def test_cascade_workspace_size():
     assert L.pkv_cascade_workspace_size(ctypes.byref(a), 0) == 0
 
 
+def test_cascade_one_launch_workspace():
+    # A decode-shaped batch (4 tokens x 8 heads of a group = 32 query rows,
+    # head size 128) runs as one balanced decode launch with the prefix as a
+    # further request: the workspace is that launch's, 1024 wave slots plus
+    # (4 + 1) x 8 item slots of 32-row fp32 partials (+ lse), and the tile
+    # prefix of 5 requests (+ 1). With a 16-row limit (head size 256) or
+    # more rows (5 tokens) the cascade is three calls, whose workspace holds
+    # both passes' outputs and lse.
+    L = pkv.lib()
+    kw = dict(num_tokens=4, num_seqs=4, num_heads=64, num_kv_heads=8, max_seqlen_q=1, max_seqlen_k=131072,
+              block_size=256, block_table_stride=512, num_blocks=4096)
+    a = good_args(**kw)
+    assert L.pkv_cascade_workspace_size(ctypes.byref(a), 32768) == (1024 + 5 * 8) * 32 * (128 + 1) * 4 + 6 * 4
+    b = good_args(**dict(kw, num_tokens=5, num_seqs=5))
+    o = (5 * 64 * 128 * 2 + 255) // 256 * 256
+    l_ = (5 * 64 * 4 + 255) // 256 * 256
+    assert L.pkv_cascade_workspace_size(ctypes.byref(b), 32768) >= 2 * (o + l_)
+    c = good_args(**dict(kw, head_size=256, num_tokens=2, num_seqs=2))  # 16 rows at head size 256: one launch
+    assert L.pkv_cascade_workspace_size(ctypes.byref(c), 32768) == (1024 + 3 * 8) * 16 * (256 + 1) * 4 + 4 * 4
+    d = good_args(**dict(kw, head_size=256))  # 32 rows at head size 256: three calls
+    assert L.pkv_cascade_workspace_size(ctypes.byref(d), 32768) >= 2 * ((4 * 64 * 256 * 2 + 255) // 256 * 256)
+
+
 @pytest.mark.parametrize("P,kw,status", [
     (0, {}, pkv.PKV_ERR_INVALID_ARG),                       # no prefix
     (100, {}, pkv.PKV_ERR_INVALID_ARG),                     # not a multiple of the page size
