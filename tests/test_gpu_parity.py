@@ -264,6 +264,22 @@ def test_cascade_equals_full_attention():
     assert_parity(out, lse, ref, ref_lse, BF16_OUT, BF16_LSE, what="cascade")
 
 
+@pytest.mark.parametrize("q_lens", [[1, 2, 1, 1], [3, 3, 2, 2]])
+def test_cascade_fp8_cache(q_lens):
+    """Over an e4m3fn cache with per-tensor scales: 5 tokens x 4 heads (20
+    query rows) run as one balanced decode launch, 10 tokens (40 rows) as the
+    two passes and the merge."""
+    prob = workloads.make_problem(611 + sum(q_lens), q_lens, [900, 300, 512, 1300], H=32, Hkv=8, hd=128, bs=16,
+                                  shared_prefix=256, cache_dtype="fp8")
+    g = GpuProblem(prob)
+    out, lse = pkv.cascade_attention(g.q, g.kc, g.vc, g.qsl, g.seq_lens, g.bt, prob.shared_prefix,
+                                     prob.max_seqlen_q, prob.max_seqlen_k, prob.scale, k_scale=g.k_scale,
+                                     v_scale=g.v_scale, return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_attention(prob)
+    assert_parity(out, lse, ref, ref_lse, FP8_OUT, BF16_LSE, what=f"cascade fp8 cache {q_lens}")
+
+
 @pytest.mark.parametrize("bs", [16, 64])
 def test_cascade_prefill_more_tokens_than_prefix(bs):
     """A chunked prefill whose 651 new tokens share a 256-key prefix: the
