@@ -893,21 +893,14 @@ __global__ __launch_bounds__(256, HD <= 128 && RB == 1 && (FP8 || HD != 128) ? 2
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued before the compute
         {
+            // every block, rows or not (a block without rows keeps an empty
+            // state): one instance of the computation per kernel, since
+            // several, chosen by the item's row count, made the compiler
+            // spill; the matrix work of empty blocks hides under the tile
+            // loads
             const uint16_t* const tile = DMA ? (const uint16_t*)(dstage + par * DT::DMA_STAGE) : stage;
-            if constexpr (RB == 1) {
-                DT::template compute<VAR, DMA>(tile, lane, c0.key0(), lo[0], limit[0], sl2, p.softcap_l2,
-                                               p.softcap_inv2, al2[0], qpos[0], qf[0], m_run[0], l_run[0],
-                                               lc_run[0], oacc[0]);
-            } else {
-                // every block, rows or not (a block without rows keeps an
-                // empty state): one instance of the computation per kernel,
-                // since several, chosen by the item's row count, made the
-                // compiler spill; the matrix work of empty blocks hides under
-                // the tile loads
-                DT::template compute_rows<VAR, DMA, RB, RB>(tile, lane, c0.key0(), lo, limit, sl2, p.softcap_l2,
-                                                            p.softcap_inv2, al2, qpos, qf, m_run, l_run, lc_run,
-                                                            oacc);
-            }
+            DT::template compute_rows<VAR, DMA, RB, RB>(tile, lane, c0.key0(), lo, limit, sl2, p.softcap_l2,
+                                                        p.softcap_inv2, al2, qpos, qf, m_run, l_run, lc_run, oacc);
         }
         if (!c1.valid || c1_new) {
             close(c0);
