@@ -311,6 +311,8 @@ pkv_status run_fwd(const pkv_varlen_args* a, const PassOpts& o, hipStream_t s) {
         const int64_t slots = pl.splits + (int64_t)a->num_seqs * a->num_kv_heads;
         p.sk_waves = pl.splits;
         p.dec_rows = pl.dec_rows;
+        // (no item has more rows than the longest request's tokens x the group)
+        p.merge_rows = (int32_t)std::min<int64_t>(pl.dec_rows, ((int64_t)a->max_seqlen_q * p.g + 7) / 8 * 8);
         p.part_o = (float*)a->workspace;
         p.part_lse = p.part_o + (size_t)slots * pl.dec_rows * a->head_size;
         p.sk_prefix = (int32_t*)(p.part_lse + (size_t)slots * pl.dec_rows);

@@ -1603,8 +1603,9 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
 }
 
 // Merge for the balanced decode schedule: one half-wave per row of a
-// (request, kv head) item, dec_rows / 8 workgroups of eight half-waves per
-// item (dec_rows = 16 RB rows). The item was covered by waves wave_of(first tile) ..
+// (request, kv head) item, merge_rows / 8 workgroups of eight half-waves per
+// item (merge_rows: the batch's longest request's rows, at most the slot's
+// 16 RB rows). The item was covered by waves wave_of(first tile) ..
 // wave_of(last tile) (those that own at least one tile); with one wave the
 // output is already final. The item comes from the block index, so the
 // metadata loads are independent of each other.
@@ -1614,7 +1615,7 @@ template <int CH>
 __global__ __launch_bounds__(256) void combine_balanced_kernel(FwdParams p) {
     const int lane = threadIdx.x & 63;
     const int hl = lane & 31;
-    const int wgs = p.dec_rows >> 3;  // workgroups per item
+    const int wgs = p.merge_rows >> 3;  // workgroups per item
     const int64_t item = blockIdx.x / wgs;
     const int r = (int)(item / p.Hkv);
     const int kh = (int)(item % p.Hkv);
@@ -1710,7 +1711,7 @@ template <int CH>
 __global__ __launch_bounds__(256) void combine_cascade_kernel(FwdParams p) {
     const int lane = threadIdx.x & 63;
     const int hl = lane & 31;
-    const int wgs = p.dec_rows >> 3;  // workgroups per item
+    const int wgs = p.merge_rows >> 3;  // workgroups per item
     const int64_t sitem = blockIdx.x / wgs;
     const int r = 1 + (int)(sitem / p.Hkv);
     const int kh = (int)(sitem % p.Hkv);
@@ -1898,8 +1899,8 @@ hipError_t launch_decode_balanced(const FwdParams& p, KvType kv, hipStream_t s) 
 }
 
 hipError_t launch_combine_balanced(const FwdParams& p, hipStream_t s) {
-    const int64_t items = (int64_t)p.B * p.Hkv;  // dec_rows / 8 workgroups per item
-    const dim3 grid((unsigned)(items * (p.dec_rows / 8)));
+    const int64_t items = (int64_t)p.B * p.Hkv;  // merge_rows / 8 workgroups per item
+    const dim3 grid((unsigned)(items * (p.merge_rows / 8)));
     // waves per item when all items are as long as the longest: chunks of
     // 16 partials pay off from about 16 partials per item
     if (p.sk_waves >= 16 * items) hipLaunchKernelGGL(combine_balanced_kernel<16>, grid, dim3(256), 0, s, p);
@@ -1908,8 +1909,8 @@ hipError_t launch_combine_balanced(const FwdParams& p, hipStream_t s) {
 }
 
 hipError_t launch_combine_cascade(const FwdParams& p, hipStream_t s) {
-    const int64_t items = (int64_t)(p.B - 1) * p.Hkv;  // suffix items; dec_rows / 8 workgroups each
-    const dim3 grid((unsigned)(items * (p.dec_rows / 8)));
+    const int64_t items = (int64_t)(p.B - 1) * p.Hkv;  // suffix items; merge_rows / 8 workgroups each
+    const dim3 grid((unsigned)(items * (p.merge_rows / 8)));
     if (p.sk_waves >= 16 * items) hipLaunchKernelGGL(combine_cascade_kernel<16>, grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL(combine_cascade_kernel<4>, grid, dim3(256), 0, s, p);
     return hipGetLastError();

@@ -33,6 +33,7 @@ struct FwdParams {
     int32_t sk_waves;         // waves sharing the decode tiles (grid = sk_waves / 4 workgroups)
     int32_t* sk_prefix;       // [B+1] per-request tile prefix and total, written by the attention kernel
     int32_t dec_rows;         // query rows per item slot (16 or 32: 16-row blocks per item)
+    int32_t merge_rows;       // rows per item the merge covers: max_seqlen_q x group, rounded up to 8, <= dec_rows
     // attention variants
     int32_t window_left;      // < 0: no sliding window
     float softcap_l2;         // softcap * log2(e) (> 0), or 0: no soft cap
