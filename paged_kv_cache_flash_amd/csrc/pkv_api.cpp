@@ -52,6 +52,11 @@ struct Plan {
     size_t workspace;  // bytes needed for `splits`
 };
 
+// Decode with a sliding window of at most this many keys, over at least this
+// many (request, kv head) items, takes the unsplit decode grid (make_plan).
+constexpr int kWindowPerItem = 1024;
+constexpr int kWindowMinItems = 256;
+
 // Query rows per balanced-decode item slot (16-row blocks) for items of
 // `rows` rows, or 0 when the balanced kernel does not take them: up to 32
 // rows over a paged cache with head size up to 128, else up to 16.
@@ -153,7 +158,19 @@ Plan make_plan(const pkv_varlen_args* a, bool balanced_ok = true) {
     int64_t items;
     int align;
     const int32_t drows = decode_rows(a, (int64_t)a->max_seqlen_q * g);
-    if (balanced_ok && mfma && !q8 && drows > 0 && a->num_splits == 0 && a->num_seqs <= kBalancedMaxSeqs) {
+    // With a short sliding window no request costs more than the window, and
+    // every request longer than it costs the same, so the plain decode grid
+    // (one workgroup per request and kv head, unsplit) is balanced by itself
+    // and needs no merge: measured faster than the balanced schedule on 64
+    // requests for every window from 128 to 2048 keys. The rule stops at
+    // kWindowPerItem keys, where a batch of one long and many short requests
+    // still costs at most a few tile rounds more than the balanced schedule,
+    // and needs enough items to give every CU a workgroup.
+    const bool short_window = a->sliding_window > 0 && a->sliding_window <= kWindowPerItem &&
+                              a->num_splits == 0 && (int64_t)a->max_seqlen_q * g <= kDecodeRows &&
+                              (int64_t)a->num_seqs * a->num_kv_heads >= kWindowMinItems;
+    if (balanced_ok && !short_window && mfma && !q8 && drows > 0 && a->num_splits == 0 &&
+        a->num_seqs <= kBalancedMaxSeqs) {
         // balanced decode: balanced_waves() waves share the KV tiles equally
         pl.kind = Kind::DecodeBalanced;
         pl.dec_rows = drows;
@@ -182,7 +199,7 @@ Plan make_plan(const pkv_varlen_args* a, bool balanced_ok = true) {
     int64_t S = 1;
     if (a->num_splits > 1) {
         S = a->num_splits;
-    } else if (a->num_splits == 0 && pl.kind != Kind::Generic) {
+    } else if (a->num_splits == 0 && pl.kind != Kind::Generic && !(short_window && pl.kind == Kind::Decode)) {
         // Split only when there are too few work items to occupy 256 CUs, and
         // keep at least 512 keys of work per split. (Prefill partials are
         // written for every query row, so splitting a prefill that already

@@ -243,6 +243,23 @@ def test_window_limits_the_split_span():
     assert L.pkv_varlen_num_splits(ctypes.byref(b)) == 6
 
 
+def test_short_window_decode_takes_the_unsplit_grid():
+    # 64 decode requests, 8 kv heads (512 items): a window of at most 1024
+    # keys bounds every item's work, so the plan is the plain decode grid,
+    # unsplit, with no workspace (no merge); a longer window, too few items,
+    # more than 16 query rows per item or a forced split keep the other plans
+    L = pkv.lib()
+    for w in (1, 128, 1024):
+        a = good_args(sliding_window=w)
+        assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 1
+        assert L.pkv_varlen_workspace_size(ctypes.byref(a)) == 0
+    assert L.pkv_varlen_num_splits(ctypes.byref(good_args(sliding_window=1025))) == 1024
+    assert L.pkv_varlen_num_splits(ctypes.byref(good_args(sliding_window=512, num_seqs=31, num_tokens=31))) == 1024
+    a = good_args(sliding_window=512, max_seqlen_q=8, num_tokens=64 * 8)  # 32 rows per item
+    assert L.pkv_varlen_num_splits(ctypes.byref(a)) == 1024
+    assert L.pkv_varlen_num_splits(ctypes.byref(good_args(sliding_window=512, num_splits=3))) == 3
+
+
 def test_forced_split_without_workspace_is_an_error():
     a = good_args(num_splits=4)
     assert pkv.lib().pkv_varlen_fwd(ctypes.byref(a), None) == pkv.PKV_ERR_WORKSPACE

@@ -134,6 +134,22 @@ def test_fp8_decode_variant(vname, bs):
     run_variant(prob, VARIANTS[vname], 0, seed=bs, what=f"fp8 decode bs={bs} {vname}")
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("window", [1, 128, 1000])
+def test_short_window_decode_grid(window, cache):
+    """A decode batch of 40 requests x 8 kv heads (320 items) with a window of
+    at most 1024 keys takes the unsplit decode grid (one workgroup per
+    request and kv head, no merge): contexts shorter and longer than the
+    window, an empty one, with sinks."""
+    rng = np.random.default_rng(960 + window)
+    ctx = rng.integers(0, 3000, 40)
+    ctx[:3] = [0, window // 2, window + 5]
+    prob = workloads.make_problem(961 + window, [1] * 40, [int(c) for c in ctx], H=32, Hkv=8, hd=128, bs=16,
+                                  cache_dtype=cache)
+    run_variant(prob, dict(sliding_window=window, sinks=True), 0, seed=window,
+                what=f"short-window decode grid w={window} {cache}")
+
+
 @pytest.mark.parametrize("vname", ["window64", "all", "alibi_all"])
 def test_fp8_prefill_variant(vname):
     prob = workloads.make_problem(951, [70, 33], [100, 0], H=8, Hkv=2, hd=128, bs=16, cache_dtype="fp8")
