@@ -49,6 +49,7 @@ struct Plan {
     int32_t split_len;
     int32_t n_qtiles;
     int32_t dec_rows;  // balanced decode: query rows per item slot
+    bool pf_ksplit;    // prefill: key-split items of kPrefillSplitRows rows
     size_t workspace;  // bytes needed for `splits`
 };
 
@@ -187,7 +188,11 @@ Plan make_plan(const pkv_varlen_args* a, bool balanced_ok = true) {
         align = kDecodeTile * kDecodeWaves;
     } else if (mfma) {
         pl.kind = Kind::Prefill;
-        const int tpw = prefill_rows(a->head_size) / g;
+        // key-split items of 64 rows when no request's rows need more (a
+        // paged cache, bf16 q, head size up to 128)
+        pl.pf_ksplit = g <= kPrefillSplitRows && (int64_t)a->max_seqlen_q * g <= kPrefillSplitRows && paged && !q8 &&
+                       a->head_size <= 128;
+        const int tpw = (pl.pf_ksplit ? kPrefillSplitRows : prefill_rows(a->head_size)) / g;
         pl.n_qtiles = (int32_t)cdiv(a->max_seqlen_q, tpw);
         items = (int64_t)a->num_seqs * a->num_kv_heads * pl.n_qtiles;
         align = prefill_tile(a->head_size) * 4;
@@ -314,6 +319,7 @@ pkv_status run_fwd(const pkv_varlen_args* a, const PassOpts& o, hipStream_t s) {
     p.num_splits = pl.splits;
     p.split_len = pl.split_len;
     p.n_qtiles = pl.n_qtiles;
+    p.pf_ksplit = pl.kind == Kind::Prefill && pl.pf_ksplit ? 1 : 0;
     p.causal = a->causal ? 1 : 0;
     p.scale_log2 = a->softmax_scale * 1.4426950408889634f;  // log2(e): kernels use exp2
     p.window_left = a->sliding_window - 1;  // -1: none

@@ -961,10 +961,17 @@ struct PfK8 {
 // the fp8 MFMA with K copied into LDS as bytes, PV stays on the bf16 MFMA
 // (V widened to bf16, P rounded to bf16: an e4m3 P would cost up to about
 // 2^-4 of a value row's magnitude per output element).
-template <int HD, bool FP8, int PG, bool VAR, bool Q8>
+// KSPLIT: work items of 64 query rows (decode-shaped batches such as
+// speculative verification): waves w and w + 2 hold the same 32 rows, wave
+// w < 2 the first 32 keys of every tile and wave w + 2 the last 32, and at
+// the end each pair folds its two running states by log-sum-exp through
+// LDS. Each wave then does half the matrix and exponential work per tile,
+// so an item's tiles pass twice as fast (the waves that a 128-row item of
+// such a batch leaves without rows would otherwise compute nothing useful).
+template <int HD, bool FP8, int PG, bool VAR, bool Q8, bool KSPLIT = false>
 __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdParams p) {
     constexpr int NW = kPrefillWaves;           // waves per workgroup
-    constexpr int ROWS = prefill_rows(HD);      // query rows per work item
+    constexpr int ROWS = KSPLIT ? kPrefillSplitRows : prefill_rows(HD);  // query rows per work item
     constexpr int TILE = prefill_tile(HD);      // keys per tile
     constexpr int CPR = HD / 8;                 // 16-byte chunks per row
     using PT = PfTile<HD>;                      // LDS tile layout
@@ -977,6 +984,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     constexpr int KS = HD / 16;                 // k-steps of S^T = K Q^T (32x32x16)
     constexpr int MB = HD / 32;                 // 32-row blocks of O^T
     constexpr int KB = TILE / 32;               // 32-key blocks per tile
+    constexpr int KBW = KSPLIT ? 1 : KB;        // 32-key blocks of a tile each wave computes
     constexpr int SLOT = TILE / PT::KPI * PT::GP;  // bytes of one K or V tile
     static_assert(TILE == kTileRows && CPW >= 1 && FCPW >= 1 && KPI == PT::KPI, "");
     static_assert(!Q8 || (FP8 && HD == 128 && FPR == 8), "the fp8 MFMA mode is built for head size 128");
@@ -990,6 +998,8 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wr = KSPLIT ? (w & 1) : w;       // the wave's group of 32 rows
+    const int kbw0 = KSPLIT ? (w >> 1) : 0;    // the wave's first 32-key block of a tile
     // Work order. Workgroup id i runs on XCD i % 8; each (request, kv head)
     // stream is pinned to XCD stream % 8 and its query tiles take consecutive
     // slots there, longest (highest) tile first, so the workgroups that share
@@ -1021,7 +1031,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
 
     // this lane's query row
     const int hsel = lane >> 5;  // which half of the 32-row MFMA tile's k dimension this lane feeds
-    const int rho = w * kPrefillRowsPerWave + (lane & 31);
+    const int rho = wr * kPrefillRowsPerWave + (lane & 31);
     const int tl = tok0 + rho / g;
     const bool row_ok = rho < tpw * g && tl < q_len;
     const int head = kh * g + rho % g;
@@ -1031,14 +1041,14 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     // keys below wave_min are visible to every valid row of the wave: tiles
     // that end there need no mask (rows past the end of the request are never
     // stored, so their scores do not matter)
-    const int wtok_first = tok0 + (w * kPrefillRowsPerWave) / g;
-    const bool wave_any = wtok_first < q_len && w * kPrefillRowsPerWave < tpw * g;
+    const int wtok_first = tok0 + (wr * kPrefillRowsPerWave) / g;
+    const bool wave_any = wtok_first < q_len && wr * kPrefillRowsPerWave < tpw * g;
     const int wave_min = !wave_any ? k_begin : (p.causal ? min(k_end, ctx + wtok_first + 1) : k_end);
     // with a sliding window, keys at or past wave_lo are visible to every
     // valid row of the wave: tiles that start there need no lower mask
     int wave_lo = 0;
     if (VAR && wave_any) {
-        const int wrho_last = min(w * kPrefillRowsPerWave + kPrefillRowsPerWave, tpw * g) - 1;
+        const int wrho_last = min(wr * kPrefillRowsPerWave + kPrefillRowsPerWave, tpw * g) - 1;
         wave_lo = window_lo(p, ctx + min(q_len - 1, tok0 + wrho_last / g));
     }
 
@@ -1197,11 +1207,12 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
 #pragma unroll
         for (int t = 0; t < 2; ++t)
             koff8[ks][t] = (lane & 31) * PfK8::RP + 16 * ((4 * ks + 2 * hsel + t) ^ PfK8::sw(lane & 31));
-    // S^T = K Q^T for one tile
-    auto qk = [&](const uint8_t* kslot, f32x16 (&sacc)[KB]) {
+    // S^T = K Q^T for the wave's key blocks of one tile
+    auto qk = [&](const uint8_t* kslot, f32x16 (&sacc)[KBW]) {
+        if constexpr (KSPLIT) kslot += kbw0 * PT::row_base(32);
         if constexpr (Q8) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
+            for (int kb = 0; kb < KBW; ++kb) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
@@ -1213,7 +1224,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
             return;
         }
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KBW; ++kb) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
@@ -1226,11 +1237,12 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     };
     // soft cap and ALiBi bias of the scores of the tile starting at key t0
     // (before the mask), taking them to the log2 domain
-    auto cap = [&](int t0, f32x16 (&sacc)[KB]) {
+    auto cap = [&](int t0, f32x16 (&sacc)[KBW]) {
+        t0 += kbw0 * 32;
         if (capped) {
             const bool sc = p.softcap_l2 > 0.f;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     float x = sacc[kb][e] * sl2_cap;
@@ -1242,12 +1254,13 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     };
     // causal / length mask of a tile that reaches past wave_min, window mask
     // of one that starts below wave_lo
-    auto mask = [&](int t0, f32x16 (&sacc)[KB]) {
-        if (t0 + TILE > wave_min || (VAR && t0 < wave_lo)) {
+    auto mask = [&](int t0, f32x16 (&sacc)[KBW]) {
+        t0 += kbw0 * 32;  // the wave's first key of the tile
+        if (t0 + 32 * KBW > wave_min || (VAR && t0 < wave_lo)) {
             const int lim = limit - t0 - hsel * 4;
             const int low = lo - t0 - hsel * 4;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int k = kb * 32 + (e >> 2) * 8 + (e & 3);
@@ -1256,10 +1269,10 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         }
     };
     // row maximum of a tile (both lane halves hold keys of the same row)
-    auto rowmax = [&](f32x16 (&sacc)[KB]) -> float {
+    auto rowmax = [&](f32x16 (&sacc)[KBW]) -> float {
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -1279,11 +1292,11 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         }
     };
     // probabilities of a tile as bf16 MFMA B operands, and their row sum
-    auto expo = [&](f32x16 (&sacc)[KB], u32x4 (&pf)[2 * KB]) {
+    auto expo = [&](f32x16 (&sacc)[KBW], u32x4 (&pf)[2 * KBW]) {
         const float nm = m_run == -INFINITY ? 0.f : -m_run;
         float ps = 0.f, pc = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KBW; ++kb) {
             float pv[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -1302,11 +1315,12 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         lc_run += pc;
     };
     // O^T += V^T P^T for one tile
-    auto pv = [&](const uint8_t* vslot, const u32x4 (&pf)[2 * KB]) {
+    auto pv = [&](const uint8_t* vslot, const u32x4 (&pf)[2 * KBW]) {
+        if constexpr (KSPLIT) vslot += kbw0 * 2 * PT::row_base(16);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int k2 = 0; k2 < 2 * KB; ++k2) {
+            for (int k2 = 0; k2 < 2 * KBW; ++k2) {
                 const int vj = pext(4 * mb, PT::SWMASK & ~3);
                 const uint8_t* vp = vslot + ((4 * mb) & ~PT::SWMASK) * 16 + k2 * PT::row_base(16);
                 const u32x2 lo = lds_read_tr16(vp + voffs[0][vj]);
@@ -1324,7 +1338,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
     // the lazy-rescale decision for it follow, after PV, so that their
     // branches stay out of that block.
     const int n_tiles = (k_end - k_begin + TILE - 1) / TILE;
-    f32x16 s_a[KB], s_b[KB];
+    f32x16 s_a[KBW], s_b[KBW];
     float mx;
     int32_t pg_v[NP];  // block-table entries of this lane's keys in tile i+1 (for V(i+1))
     int32_t pg_k[NP];  // block-table entries of this lane's keys in tile i+2 (for K(i+2))
@@ -1352,7 +1366,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         rescale(mx);
         __syncthreads();
     }
-    auto iteration = [&](auto par, auto last, int i, f32x16 (&sc)[KB], f32x16 (&sn)[KB]) {
+    auto iteration = [&](auto par, auto last, int i, f32x16 (&sc)[KBW], f32x16 (&sn)[KBW]) {
         constexpr int P = decltype(par)::value;
         constexpr bool LAST = decltype(last)::value;
         uint8_t* const k_here = P ? k_lds1 : k_lds0;   // K(i), now free: receives K(i+2)
@@ -1369,7 +1383,7 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
             issue(p.v_cache, t0 + TILE, pg_v, v_next, st_v, false);
             if (i + 3 < n_tiles) page_of(t0 + 3 * TILE, pg_k);
         }
-        u32x4 pf[2 * KB];
+        u32x4 pf[2 * KBW];
         if constexpr (!LAST) qk(k_next, sn);
         expo(sc, pf);
         pv(v_here, pf);
@@ -1405,6 +1419,38 @@ __global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_kernel(FwdPara
         iteration(I0{}, std::true_type{}, i, s_a, s_b);
     }
 
+    if constexpr (KSPLIT) {
+        // Waves 2 and 3 hand their running state (output accumulators in
+        // a K slot, m / l / lc in a V slot, lane-contiguous) to the wave
+        // that holds the same rows, which folds both by log-sum-exp; the
+        // tile slots are free once every wave is past the loop.
+        static_assert(MB * 16 * 64 * 4 <= SLOT && 3 * 64 * 4 <= SLOT, "the pair's state fits one slot");
+        __syncthreads();
+        float* const po = (float*)(wr ? k_lds1 : k_lds0);
+        float* const ps = (float*)(wr ? v_lds1 : v_lds0);
+        if (w >= 2) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) po[(mb * 16 + e) * 64 + lane] = oacc[mb][e];
+            ps[lane] = m_run;
+            ps[64 + lane] = l_run;
+            ps[128 + lane] = lc_run;
+        }
+        __syncthreads();
+        if (w >= 2) return;
+        const float mb_ = ps[lane], lb = ps[64 + lane], lcb = ps[128 + lane];
+        const float m_new = fmaxf(m_run, mb_);
+        const float mr = m_new == -INFINITY ? 0.f : m_new;
+        const float a = fast_exp2(m_run - mr), b = fast_exp2(mb_ - mr);  // 0 for a side with no key yet
+        l_run = a * l_run + b * lb;
+        lc_run = a * lc_run + b * lcb;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[mb][e] = a * oacc[mb][e] + b * po[(mb * 16 + e) * 64 + lane];
+        m_run = m_new;
+    }
     if (!row_ok) return;
     l_run += __shfl_xor(l_run, 32);
     lc_run += __shfl_xor(lc_run, 32);
@@ -1941,6 +1987,21 @@ static hipError_t prefill_hd(const FwdParams& p, KvType kv, bool q8, hipStream_t
         }
     }
     if (q8) return hipErrorInvalidValue;
+    if (p.pf_ksplit) {  // items of 64 rows over a paged cache, head size <= 128
+        if constexpr (HD <= 128) {
+            if (pg == kPgFlat) return hipErrorInvalidValue;
+            if (kv == KvType::FP8) {
+                if (pg == kPgWide) launch_var((prefill_kernel<HD, true, kPgWide, true, false, true>), (prefill_kernel<HD, true, kPgWide, false, false, true>), var, grid, s, p);
+                else launch_var((prefill_kernel<HD, true, kPgAny, true, false, true>), (prefill_kernel<HD, true, kPgAny, false, false, true>), var, grid, s, p);
+            } else {
+                if (pg == kPgWide) launch_var((prefill_kernel<HD, false, kPgWide, true, false, true>), (prefill_kernel<HD, false, kPgWide, false, false, true>), var, grid, s, p);
+                else launch_var((prefill_kernel<HD, false, kPgAny, true, false, true>), (prefill_kernel<HD, false, kPgAny, false, false, true>), var, grid, s, p);
+            }
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     if (kv == KvType::FP8) {
         if (pg == kPgFlat) launch_var((prefill_kernel<HD, true, kPgFlat, true, false>), (prefill_kernel<HD, true, kPgFlat, false, false>), var, grid, s, p);
         else if (pg == kPgWide) launch_var((prefill_kernel<HD, true, kPgWide, true, false>), (prefill_kernel<HD, true, kPgWide, false, false>), var, grid, s, p);

@@ -33,6 +33,7 @@ struct FwdParams {
     int32_t sk_waves;         // waves sharing the decode tiles (grid = sk_waves / 4 workgroups)
     int32_t* sk_prefix;       // [B+1] per-request tile prefix and total, written by the attention kernel
     int32_t dec_rows;         // query rows per item slot (16 or 32: 16-row blocks per item)
+    int32_t pf_ksplit;        // prefill kernel: items of kPrefillSplitRows rows, two waves per 32 rows
     int32_t merge_rows;       // rows per item the merge covers: max_seqlen_q x group, rounded up to 8, <= dec_rows
     // attention variants
     int32_t window_left;      // < 0: no sliding window
@@ -126,6 +127,10 @@ constexpr int kXcds = 8;
 // K/V tiles of 64 keys in LDS (two workgroups per CU up to head size 128).
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillWaves = 4;
+// Query rows per work item of the prefill kernel's key-split mode (two waves
+// per 32 rows, each on half of every tile), taken when no item of a paged
+// batch has more rows than this.
+constexpr int kPrefillSplitRows = 64;
 constexpr int prefill_tile(int) { return 64; }
 constexpr int prefill_rows(int) { return kPrefillRowsPerWave * kPrefillWaves; }
 // The largest GQA group the prefill kernel packs (query rows per workgroup).
