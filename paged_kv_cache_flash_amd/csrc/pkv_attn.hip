@@ -19,16 +19,32 @@
 //                  Four waves share the item's key range; K goes straight from
 //                  HBM into MFMA registers, V is staged in LDS and read back
 //                  transposed; the waves merge their states through LDS.
+//  decode_balanced_kernel
+//                  the 32-key tiles of every (request, kv head) item laid end
+//                  to end and dealt out in equal contiguous shares to a grid of
+//                  waves that is resident at once; items of up to 32 query rows
+//                  as one or two 16-column blocks of the 16x16x32 MFMA, tiles
+//                  copied straight into LDS (two stages per wave), one partial
+//                  state per item segment a wave covers (a whole item: the
+//                  final output).
 //  prefill_kernel  one work item = (request, kv head, 128 query rows, KV split);
-//                  rows are (token, head-of-group) pairs, 32 per wave, on
-//                  32x32x16 bf16 MFMA; 64-key K/V tiles are copied from HBM
-//                  straight into padded chunk-major LDS (two slots each, one
-//                  tile ahead) and shared by the four waves; only tiles crossing the diagonal
-//                  build a per-element mask.
+//                  rows are (token, head-of-group) pairs, 32 per wave, on the
+//                  32x32x16 bf16 MFMA (32x32x64 fp8 for Q K^T with an fp8 q);
+//                  64-key K/V tiles are copied from HBM straight into padded
+//                  row-major LDS (16-byte chunks permuted per row; two slots
+//                  each, one tile ahead) and shared by the four waves; only
+//                  tiles crossing the diagonal build a per-element mask. Items
+//                  of at most 64 rows run key-split: two waves per 32 rows, each
+//                  on one 32-key half of every tile, folded at the end.
 //  generic_kernel  one wave per (token, head); plain fp32 arithmetic on the
 //                  vector ALUs for fp32 inputs and head sizes without an MFMA
 //                  instantiation.
-//  combine_kernel  log-sum-exp merge of the split partials.
+//  combine_kernel  log-sum-exp merge of the KV-split partials of the above.
+//  combine_balanced_kernel
+//                  log-sum-exp merge of the balanced decode's partial states.
+//  combine_cascade_kernel
+//                  the same for a cascade run as one balanced decode: each
+//                  suffix row folded with the shared-prefix item's row.
 //  merge_kernel    merge of two attention states (cascade prefix / suffix).
 #include <type_traits>
 
