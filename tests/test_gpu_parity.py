@@ -194,6 +194,23 @@ def test_generic_parity(case, num_splits):
     run_and_check(prob, num_splits, what=f"generic {case}")
 
 
+@pytest.mark.parametrize("B,q", [(1024, 1), (1024, 8), (1100, 1)])
+def test_decode_many_requests(B, q):
+    """The balanced schedule's largest batch (1024 requests; its scan walks
+    the requests 64 at a time), with one and two 16-row blocks per item, and
+    one request more, which the per-item decode grid takes instead: short
+    mixed contexts, some empty, every row against the oracle."""
+    rng = np.random.default_rng(B + q)
+    ctx = rng.integers(0, 300, B)
+    ctx[::97] = 0
+    prob = workloads.make_problem(5000 + B + q, [q] * B, [int(c) for c in ctx], H=8, Hkv=2, hd=64, bs=16)
+    g = GpuProblem(prob)
+    out, lse = g.run(num_splits=0)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_attention(prob)
+    assert_parity(out, lse, ref, ref_lse, *tol(prob), what=f"decode of {B} requests x {q} tokens")
+
+
 @pytest.mark.parametrize("bs", [1, 8, 16, 64, 256])
 def test_fp8_cache_decode_parity(bs):
     prob = workloads.make_problem(500, [1] * 6, [40, 300, 1023, 7, 260, 513], H=32, Hkv=8, hd=128, bs=bs,
