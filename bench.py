@@ -16,7 +16,8 @@ second (GB/s) against the MI355X HBM peak of 8 TB/s; and, nested under
 "prefill" in the same JSON line, chunked prefill (batch 8, new tokens uniform
 in [128, 2048] on cached contexts uniform in [0, 4096], same heads, page 16,
 causal) in TFLOP/s of visible query-key pairs against the 2.5 PFLOP/s bf16
-dense MFMA peak.
+dense MFMA peak. Under "also", the other workloads below (20 timed steps
+each, no CPU baseline), each run as a child process.
 Other workloads (--workload): chunked_prefill (TFLOP/s against the 2.5 PFLOP/s
 bf16 dense MFMA peak), long_decode, long_decode_cascade, fp8_decode,
 spec_decode (several new tokens per request; KV GB/s). The
@@ -587,6 +588,44 @@ def run_one(args, wl):
     return line
 
 
+# The other workloads of the hot path, timed briefly in the default run, each
+# in a child process of its own (so that no failure there costs the line
+# above): configs 4 and 5, config 4 as a one-launch cascade, multi-token
+# decode, the non-causal encoder and windowed decode with sinks.
+OTHER_WORKLOADS = (("long_decode", ["--workload", "long_decode"]),
+                   ("long_decode_cascade", ["--workload", "long_decode_cascade"]),
+                   ("fp8_decode", ["--workload", "fp8_decode"]),
+                   ("multi_token_decode", ["--workload", "spec_decode"]),
+                   ("encoder", ["--workload", "encoder"]),
+                   ("paged_decode_window1024_sinks", ["--workload", "paged_decode", "--sliding-window", "1024",
+                                                      "--sinks"]))
+
+
+def other_workloads():
+    import subprocess
+    out = {}
+    for key, wargs in OTHER_WORKLOADS:
+        cmd = [sys.executable, os.path.abspath(__file__), *wargs, "--steps", "20", "--warmup", "5",
+               "--no-cpu-baseline"]
+        log(f"[bench] {key}: {' '.join(wargs)}")
+        try:
+            res = subprocess.run(cmd, capture_output=True, text=True, timeout=180)
+            rows = [l for l in res.stdout.splitlines() if l.startswith("{")]
+            if res.returncode != 0 or not rows:
+                tail = (res.stderr or res.stdout).strip().splitlines()[-1:] or [""]
+                out[key] = {"error": f"exit {res.returncode}: {tail[0][:200]}"}
+                continue
+            r = json.loads(rows[-1])
+            rf = r["roofline"]
+            out[key] = {"metric": r["metric"], "value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"],
+                        "steps": r["steps"], "config": r["config"],
+                        "roofline": {k: rf.get(k) for k in ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                                            "attention_ms_per_call_graph")}}
+        except Exception as e:  # (a timeout, an unreadable line)
+            out[key] = {"error": f"{type(e).__name__}: {e}"[:200]}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -648,6 +687,7 @@ def main():
         pre = run_one(args, "chunked_prefill")
         line["prefill"] = {k: pre[k] for k in ("metric", "value", "unit", "ms_per_step", "higher_is_better",
                                                 "dtype", "config", "roofline", "cpu_baseline", "cache_write")}
+        line["also"] = other_workloads()
     else:
         line = run_one(args, args.workload)
     print(json.dumps(line), flush=True)
